@@ -1,0 +1,13 @@
+"""CPU fp64 oracle (test infrastructure only; never used by the product path)."""
+from .attention import (  # noqa: F401
+    ALIBI_GEOMETRIC,
+    ALIBI_NONE,
+    ALIBI_PAGE1,
+    alibi_slopes,
+    apply_rope,
+    attention_decode,
+    attention_prefill,
+    kv_bytes_per_token,
+    prefill_flops,
+    rope_inv_freq,
+)

@@ -1,0 +1,364 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself.
+
+* brute force: scalar Python loops that rotate with complex numbers and
+  normalise with math.fsum, all flag combinations, tiny sizes;
+* a library routine: torch's scaled_dot_product_attention in fp64 on the CPU
+  (the routine the Flash-Attention page tests against), with RoPE applied by
+  torch's complex polar form and ALiBi passed as a float mask;
+* the lab page's two printed property values on its seeded instance;
+* closed forms (prefix mean for Q = 0, geometric ALiBi weights, T = 1, constant V);
+* invariants (rotation norm, the relative-position identity of the RoPE
+  equation, GQA == MHA with repeated K/V, incremental decode == full);
+* negative tests from the lab's "break it on purpose" exercise.
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import (
+    ALIBI_GEOMETRIC,
+    ALIBI_NONE,
+    ALIBI_PAGE1,
+    alibi_slopes,
+    apply_rope,
+    attention_decode,
+    attention_prefill,
+    kv_bytes_per_token,
+    prefill_flops,
+)
+from transformer_attention_02_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- brute force
+def brute_attention(q, k, v, pos0, base, causal, alibi):
+    """Scalar loops. RoPE as multiplication of (x0 + i x1) by e^{i p theta}
+    (the complex form of the RoPE equation on the transformer-from-scratch page);
+    the softmax as exp / fsum without max subtraction; heads grouped by repetition."""
+    B, H, T, hd = q.shape
+    KV = k.shape[1]
+    kv_of = [g for g in range(KV) for _ in range(H // KV)]
+    if alibi == ALIBI_GEOMETRIC:
+        slope = [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
+    elif alibi == ALIBI_PAGE1:
+        slope = [1.0 / 2.0 ** (2.0 * (h + 1) / H) for h in range(H)]
+    else:
+        slope = [0.0] * H
+
+    def rot(vec, p):
+        if base == 0:
+            return [float(x) for x in vec]
+        outv = []
+        for i in range(hd // 2):
+            theta = base ** (-(2.0 * i) / hd)
+            z = complex(vec[2 * i], vec[2 * i + 1]) * cmath.exp(1j * p * theta)
+            outv += [z.real, z.imag]
+        return outv
+
+    out = np.zeros((B, H, T, hd))
+    lse = np.zeros((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            g = kv_of[h]
+            keys = [rot(k[b, g, j], pos0 + j) for j in range(T)]
+            for i in range(T):
+                qi = rot(q[b, h, i], pos0 + i)
+                js = [j for j in range(T) if (j <= i or not causal)]
+                sc = [math.fsum(a * c for a, c in zip(qi, keys[j])) / math.sqrt(hd) - slope[h] * abs(i - j)
+                      for j in js]
+                ex = [math.exp(s) for s in sc]
+                z = math.fsum(ex)
+                for d in range(hd):
+                    out[b, h, i, d] = math.fsum(e * v[b, g, j, d] for e, j in zip(ex, js)) / z
+                lse[b, h, i] = math.log(z)
+    return out, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("alibi", [ALIBI_NONE, ALIBI_GEOMETRIC, ALIBI_PAGE1])
+@pytest.mark.parametrize("base,pos0", [(0.0, 0), (10000.0, 0), (10000.0, 7), (500000.0, 100)])
+@pytest.mark.parametrize("H,KV", [(4, 2), (3, 1), (2, 2)])
+def test_prefill_matches_brute_force(causal, alibi, base, pos0, H, KV):
+    rng = np.random.default_rng(hash((causal, alibi, base, pos0, H, KV)) % 2**32)
+    B, T, hd = 2, 5, 6
+    q = rng.normal(size=(B, H, T, hd))
+    k = rng.normal(size=(B, KV, T, hd))
+    v = rng.normal(size=(B, KV, T, hd))
+    out, lse = attention_prefill(q, k, v, pos0=pos0, rope_base=base, causal=causal, alibi=alibi)
+    ref, ref_lse = brute_attention(q, k, v, pos0, base, causal, alibi)
+    assert np.abs(out - ref).max() < 1e-13
+    assert np.abs(lse - ref_lse).max() < 1e-13
+
+
+# ------------------------------------------------------- library routine (SDPA)
+def torch_rope(x, pos0, base):
+    """RoPE via torch's complex polar form (a separate formulation from the oracle's)."""
+    hd = x.shape[-1]
+    T = x.shape[-2]
+    inv = 1.0 / (base ** (torch.arange(0, hd, 2, dtype=torch.float64) / hd))
+    ang = torch.outer(torch.arange(pos0, pos0 + T, dtype=torch.float64), inv)
+    rotor = torch.polar(torch.ones_like(ang), ang)
+    xc = torch.view_as_complex(x.reshape(*x.shape[:-1], hd // 2, 2).contiguous())
+    return torch.view_as_real(xc * rotor).flatten(-2)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("alibi", [ALIBI_NONE, ALIBI_GEOMETRIC])
+@pytest.mark.parametrize("base", [0.0, 10000.0])
+def test_prefill_matches_torch_sdpa(causal, alibi, base):
+    g = torch.Generator().manual_seed(11)
+    B, H, KV, T, hd = 2, 8, 2, 33, 16
+    q = torch.randn(B, H, T, hd, generator=g, dtype=torch.float64)
+    k = torch.randn(B, KV, T, hd, generator=g, dtype=torch.float64)
+    v = torch.randn(B, KV, T, hd, generator=g, dtype=torch.float64)
+    pos0 = 3
+    qr, kr = (torch_rope(q, pos0, base), torch_rope(k, pos0, base)) if base else (q, k)
+    mask = None
+    if alibi:
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float64)
+        i = torch.arange(T, dtype=torch.float64)
+        mask = -slopes[:, None, None] * (i[:, None] - i[None, :]).abs()
+        if causal:
+            mask = mask.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+    ref = F.scaled_dot_product_attention(qr, kr, v, attn_mask=mask, is_causal=causal and mask is None,
+                                         enable_gqa=True)
+    out, _ = attention_prefill(q.numpy(), k.numpy(), v.numpy(), pos0=pos0, rope_base=base,
+                               causal=causal, alibi=alibi)
+    assert np.abs(out - ref.numpy()).max() < 1e-12
+
+
+# ---------------------------------------------------- the lab page's properties
+def lab_forward(x, pos0, causal=True, rotate_v=False):
+    _, Wq, Wk, Wv, Wo = W.lab_instance()
+    q = W.split_heads(x @ Wq, 4)
+    k = W.split_heads(x @ Wk, 2)
+    v = W.split_heads(x @ Wv, 2)
+    if rotate_v:
+        v = apply_rope(v, pos0 + np.arange(x.shape[0]), 10000.0)
+    out, _ = attention_prefill(q, k, v, pos0=pos0, rope_base=10000.0, causal=causal)
+    T = x.shape[0]
+    return out[0].transpose(1, 0, 2).reshape(T, -1) @ Wo
+
+
+def test_lab_printed_properties():
+    gold = json.load(open(os.path.join(GOLDEN, "lab_properties.json")))
+    x = W.lab_instance()[0]
+    base_out = lab_forward(x, 0)
+    x2 = x.copy()
+    x2[-1] += 1.0
+    causal_check = np.abs(lab_forward(x2, 0)[:-1] - base_out[:-1]).max()
+    relative_check = np.abs(lab_forward(x, 100) - base_out).max()
+    assert causal_check == gold["causal_check"]["value"]        # exactly 0.0
+    assert relative_check < 10 * gold["relative_check"]["value"]  # about 1e-15
+    assert relative_check > 0.0                                 # rotation really happened
+
+
+def test_lab_break_it_on_purpose():
+    """Exercise 1: without the mask property 1 fails; rotating V breaks property 2."""
+    x = W.lab_instance()[0]
+    x2 = x.copy()
+    x2[-1] += 1.0
+    assert np.abs(lab_forward(x2, 0, causal=False)[:-1] - lab_forward(x, 0, causal=False)[:-1]).max() > 1e-3
+    assert np.abs(lab_forward(x, 100, rotate_v=True) - lab_forward(x, 0, rotate_v=True)).max() > 1e-3
+
+
+def test_tiny_fp32_inputs_are_the_lab_instance():
+    q, k, v = W.tiny_qkv()
+    x, Wq, Wk, Wv, _ = W.lab_instance()
+    assert q.dtype == np.float32 and q.shape == (1, 4, 6, 8) and k.shape == (1, 2, 6, 8)
+    assert np.array_equal(q[0, 1, 3], (x @ Wq)[3, 8:16].astype(np.float32))
+    assert np.array_equal(v[0, 1, 5], (x @ Wv)[5, 8:16].astype(np.float32))
+
+
+# ------------------------------------------------------------------ closed forms
+def _rand(shape, seed):
+    return np.random.default_rng(seed).normal(size=shape)
+
+
+@pytest.mark.parametrize("base", [0.0, 10000.0])
+def test_zero_query_gives_prefix_mean(base):
+    B, H, KV, T, hd = 1, 4, 2, 9, 8
+    v = _rand((B, KV, T, hd), 1)
+    out, lse = attention_prefill(np.zeros((B, H, T, hd)), _rand((B, KV, T, hd), 2), v, rope_base=base)
+    for h in range(H):
+        prefix = np.cumsum(v[0, h // 2], axis=0) / np.arange(1, T + 1)[:, None]
+        assert np.abs(out[0, h] - prefix).max() < 1e-14
+    assert np.abs(lse[0, 0] - np.log(np.arange(1, T + 1))).max() < 1e-14
+
+
+def test_zero_query_alibi_gives_geometric_weights():
+    B, H, T, hd = 1, 4, 7, 4
+    v = _rand((B, H, T, hd), 3)
+    out, _ = attention_prefill(np.zeros((B, H, T, hd)), _rand((B, H, T, hd), 4), v, rope_base=0.0,
+                               alibi=ALIBI_GEOMETRIC)
+    for h in range(H):
+        r = math.exp(-(2.0 ** (-8.0 * (h + 1) / H)))
+        for i in range(T):
+            w = np.array([r ** (i - j) for j in range(i + 1)])
+            assert np.abs(out[0, h, i] - (w / w.sum()) @ v[0, h, : i + 1]).max() < 1e-14
+
+
+def test_first_row_single_token_and_constant_v():
+    B, H, KV, T, hd = 2, 4, 1, 5, 8
+    q, k, v = _rand((B, H, T, hd), 5), _rand((B, KV, T, hd), 6), _rand((B, KV, T, hd), 7)
+    out, _ = attention_prefill(q, k, v, rope_base=10000.0, pos0=9, alibi=ALIBI_GEOMETRIC)
+    assert np.array_equal(out[:, :, 0], np.repeat(v[:, :, 0], H // KV, axis=1))
+    one, _ = attention_prefill(q[:, :, :1], k[:, :, :1], v[:, :, :1], rope_base=10000.0)
+    assert np.array_equal(one[:, :, 0], np.repeat(v[:, :, 0], H // KV, axis=1))
+    const = np.broadcast_to(np.arange(hd, dtype=np.float64), (B, KV, T, hd))
+    outc, _ = attention_prefill(q, k, const, rope_base=10000.0, causal=False)
+    assert np.abs(outc - np.arange(hd)).max() < 1e-13
+
+
+# ------------------------------------------------------------------- RoPE pins
+def test_rope_identity_norm_and_relative_identity():
+    x = _rand((3, 16), 8)
+    assert np.array_equal(apply_rope(x, [0, 0, 0], 10000.0), x)
+    y = apply_rope(x, [5, 77, 4000], 10000.0)
+    assert np.abs(np.hypot(y[:, 0::2], y[:, 1::2]) - np.hypot(x[:, 0::2], x[:, 1::2])).max() < 1e-14
+    # <R(m) q, R(n) k> = <R(m-n) q, k>: the relative-position identity of the RoPE equation
+    qv, kv = _rand((1, 16), 9), _rand((1, 16), 10)
+    for m, n in [(0, 0), (5, 3), (100, 900), (4095, 17)]:
+        lhs = (apply_rope(qv, [m], 500000.0) @ apply_rope(kv, [n], 500000.0).T)[0, 0]
+        rhs = (apply_rope(qv, [m - n], 500000.0) @ kv.T)[0, 0]
+        assert abs(lhs - rhs) < 1e-12
+
+
+def test_rope_matches_complex_form():
+    x = _rand((2, 5, 32), 12)
+    ref = torch_rope(torch.from_numpy(x), 41, 10000.0).numpy()
+    assert np.abs(apply_rope(x, 41 + np.arange(5), 10000.0) - ref).max() < 1e-12
+
+
+def test_rope_pairs_are_interleaved_not_halves():
+    """Pair (0, 1) rotates together: a vector with only x[0] set keeps x[2:] zero."""
+    x = np.zeros((1, 8))
+    x[0, 0] = 1.0
+    y = apply_rope(x, [1], 10000.0)
+    assert abs(y[0, 0] - math.cos(1.0)) < 1e-15 and abs(y[0, 1] - math.sin(1.0)) < 1e-15
+    assert np.all(y[0, 2:] == 0.0)
+
+
+def test_alibi_slopes():
+    assert np.allclose(alibi_slopes(16, ALIBI_GEOMETRIC), [2.0 ** (-(h + 1) / 2.0) for h in range(16)], rtol=0, atol=0)
+    s8 = alibi_slopes(8, ALIBI_GEOMETRIC)
+    assert s8[0] == 0.5 and s8[-1] == 2.0 ** -8
+    assert np.array_equal(alibi_slopes(4, ALIBI_PAGE1), [2.0 ** -0.5, 0.5, 2.0 ** -1.5, 0.25])
+
+
+# --------------------------------------------------------------------- GQA pin
+def test_gqa_equals_mha_with_repeated_kv():
+    B, H, KV, T, hd = 2, 8, 2, 11, 8
+    q, k, v = _rand((B, H, T, hd), 13), _rand((B, KV, T, hd), 14), _rand((B, KV, T, hd), 15)
+    out, lse = attention_prefill(q, k, v, rope_base=10000.0, pos0=4, alibi=ALIBI_GEOMETRIC)
+    out2, lse2 = attention_prefill(q, np.repeat(k, H // KV, axis=1), np.repeat(v, H // KV, axis=1),
+                                   rope_base=10000.0, pos0=4, alibi=ALIBI_GEOMETRIC)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_row_sampling_matches_full():
+    B, H, KV, T, hd = 2, 4, 2, 13, 8
+    q, k, v = _rand((B, H, T, hd), 16), _rand((B, KV, T, hd), 17), _rand((B, KV, T, hd), 18)
+    full, lse = attention_prefill(q, k, v, rope_base=10000.0, pos0=2)
+    rows = [(1, 3, 12), (0, 0, 0), (0, 2, 7), (1, 3, 5)]
+    part, plse = attention_prefill(q, k, v, rope_base=10000.0, pos0=2, rows=rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.abs(part[n] - full[b, h, i]).max() < 1e-15
+        assert abs(plse[n] - lse[b, h, i]) < 1e-15
+
+
+# ------------------------------------------------------------------ decode pins
+@pytest.mark.parametrize("alibi", [ALIBI_NONE, ALIBI_GEOMETRIC])
+def test_incremental_decode_equals_full(alibi):
+    """Lab exercise 2: token-by-token with a cache reproduces the full computation."""
+    B, H, KV, T, hd = 2, 4, 2, 9, 8
+    q, k, v = _rand((B, H, T, hd), 19), _rand((B, KV, T, hd), 20), _rand((B, KV, T, hd), 21)
+    full, full_lse = attention_prefill(q, k, v, rope_base=10000.0, alibi=alibi)
+    kc = np.zeros((B, KV, T, hd))
+    vc = np.zeros((B, KV, T, hd))
+    for t in range(T):
+        lens = np.full(B, t, dtype=np.int32)
+        out, lse, ks, vs = attention_decode(q[:, :, t], k[:, :, t], v[:, :, t], kc, vc, lens,
+                                            rope_base=10000.0, alibi=alibi)
+        kc[:, :, t], vc[:, :, t] = ks, vs
+        assert np.abs(out - full[:, :, t]).max() < 1e-13
+        assert np.abs(lse - full_lse[:, :, t]).max() < 1e-13
+
+
+def test_decode_ragged_lengths_and_batch_subset():
+    B, H, KV, hd, Lmax = 3, 4, 1, 8, 12
+    q, kn, vn = _rand((B, H, hd), 22), _rand((B, KV, hd), 23), _rand((B, KV, hd), 24)
+    kc, vc = _rand((B, KV, Lmax, hd), 25), _rand((B, KV, Lmax, hd), 26)
+    lens = np.array([0, 5, 11], dtype=np.int32)
+    out, lse, ks, _ = attention_decode(q, kn, vn, kc, vc, lens, rope_base=10000.0)
+    # length 0: the only key is the token itself -> output is v_new
+    assert np.array_equal(out[0], np.repeat(vn[0], H, axis=0))
+    assert abs(np.hypot(ks[2, 0, 0::2], ks[2, 0, 1::2]) - np.hypot(kn[2, 0, 0::2], kn[2, 0, 1::2])).max() < 1e-14
+    out2, _, _, _ = attention_decode(q, kn, vn, kc, vc, lens, rope_base=10000.0, batch=[2, 1])
+    assert np.array_equal(out2[0], out[2]) and np.array_equal(out2[1], out[1])
+
+
+def tiled_online_softmax(qr, kr, v, scale, block, causal_row):
+    """fp64 restatement of the Flash-Attention page's Step 3 recurrence for one query row
+    (running max m, denominator l, rescaled accumulator), with causal key skipping."""
+    m, l, acc = -math.inf, 0.0, np.zeros(v.shape[1])
+    n = kr.shape[0] if causal_row is None else causal_row + 1
+    for s in range(0, n, block):
+        e = min(s + block, n)
+        sc = (kr[s:e] @ qr) * scale
+        m_new = max(m, sc.max())
+        alpha = math.exp(m - m_new) if m != -math.inf else 0.0
+        p = np.exp(sc - m_new)
+        l = alpha * l + p.sum()
+        acc = alpha * acc + p @ v[s:e]
+        m = m_new
+    return acc / l, m + math.log(l)
+
+
+def test_tiled_online_softmax_and_split_merge_equal_definition():
+    """The kernel's recurrence (tiled, and split into partials merged by log-sum-exp)
+    reproduces the oracle: the rearrangement the GPU relies on is exact up to rounding."""
+    T, hd = 37, 8
+    q, k, v = _rand((1, 1, T, hd), 27), _rand((1, 1, T, hd), 28), _rand((1, 1, T, hd), 29)
+    out, lse = attention_prefill(q, k, v, rope_base=10000.0)
+    qr = apply_rope(q[0, 0], np.arange(T), 10000.0)
+    kr = apply_rope(k[0, 0], np.arange(T), 10000.0)
+    for block in (1, 4, 16, 64):
+        for i in (0, 5, 36):
+            o, ls = tiled_online_softmax(qr[i], kr, v[0, 0], 1 / math.sqrt(hd), block, i)
+            assert np.abs(o - out[0, 0, i]).max() < 1e-14 and abs(ls - lse[0, 0, i]) < 1e-13
+    # split the 37 keys of the last row into chunks, then merge the partials by LSE
+    i = T - 1
+    parts = [tiled_online_softmax(qr[i], kr[s:s + 10], v[0, 0, s:s + 10], 1 / math.sqrt(hd), 64, None)
+             for s in range(0, T, 10)]
+    M = max(p[1] for p in parts)
+    wts = [math.exp(p[1] - M) for p in parts]
+    merged = sum(w * p[0] for w, p in zip(wts, parts)) / sum(wts)
+    assert np.abs(merged - out[0, 0, i]).max() < 1e-14
+
+
+# --------------------------------------------------------------- counting pins
+def test_cache_count_exercise():
+    """Lab exercise 4: KV=2, hd=8 -> 2*2*8 = 32 numbers per token per layer; MHA (4 heads) 64."""
+    assert kv_bytes_per_token(2, 8, 1) == 32
+    assert kv_bytes_per_token(4, 8, 1) == 64
+
+
+def test_prefill_flop_count():
+    for T in (1, 2, 7):
+        pairs = sum(1 for i in range(T) for j in range(T) if j <= i)
+        assert prefill_flops(2, 3, T, 8) == 4 * 2 * 3 * 8 * pairs
+    assert W.LLAMA3_8B.flops() == pytest.approx(5.4992e11, rel=1e-4)
+
+
+def test_decode_workload_lengths():
+    lens = W.KV_DECODE.lengths()
+    assert len(lens) == 64 and lens.min() >= 512 and lens.max() <= 8192
+    assert W.KV_DECODE.kv_read_bytes() == int((lens.astype(np.int64) + 1).sum()) * 8 * 128 * 4

@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs and the workload table.
+
+This module draws random numbers and nothing else: it holds none of the
+attention arithmetic (no rotation, no softmax, no masking), so the HIP path and
+the CPU oracle can both be fed from it without sharing any of the method.
+
+Every tensor is produced on the host from a fixed seed:
+
+* the tiny fp32 case is the seeded instance of the "Write attention from
+  scratch" lab page (NumPy ``default_rng(0)``; draws x, Wq, Wk, Wv, Wo in that
+  order, weights scaled by 1/sqrt(d)); its Q/K/V are ``x @ W`` in fp64, split
+  into heads and stored as fp32;
+* the bf16 cases draw fp32 N(0,1) from ``torch.Generator().manual_seed(seed)``
+  in the order q, k, v and round each value to bf16 (round to nearest even);
+* the decode case draws context lengths with NumPy ``default_rng(5)``
+  (integers in [512, 8192], both ends inclusive), then q, k_new, v_new and the
+  valid prefix of each sequence's K/V cache from a torch generator; cache rows
+  at or past a sequence's length are zero and are never read.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    T: int
+    H: int
+    KV: int
+    hd: int
+    dtype: str
+    seed: int
+    rope_base: float  # 0.0 means no rotary embedding
+    pos0: int = 0
+    causal: bool = True
+    alibi: int = 0  # 0 none, 1 geometric 2^(-8(h+1)/H), 2 page-1 heuristic 2^(-2(h+1)/H)
+
+    def flops(self) -> float:
+        """Algorithmic flops: two contractions over the visible (query, key) pairs."""
+        pairs = self.T * (self.T + 1) // 2 if self.causal else self.T * self.T
+        return 4.0 * self.B * self.H * self.hd * pairs
+
+    def io_bytes(self, out_elem: int = 4) -> int:
+        e = 4 if self.dtype == F32 else 2
+        return (self.B * self.H * self.T * self.hd * (e + out_elem)
+                + 2 * self.B * self.KV * self.T * self.hd * e)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    KV: int
+    hd: int
+    len_lo: int
+    len_hi: int
+    len_seed: int
+    seed: int
+    rope_base: float
+    alibi: int = 0
+    dtype: str = BF16
+
+    def lengths(self) -> np.ndarray:
+        rng = np.random.default_rng(self.len_seed)
+        return rng.integers(self.len_lo, self.len_hi, size=self.B, endpoint=True).astype(np.int32)
+
+    def lmax(self) -> int:
+        return int(self.lengths().max()) + 1
+
+    def kv_read_bytes(self) -> int:
+        """K and V bytes the step must read: (len_b + 1) rows of K and V per KV head."""
+        e = 4 if self.dtype == F32 else 2
+        return int(sum(int(L) + 1 for L in self.lengths()) * self.KV * self.hd * 2 * e)
+
+
+TINY_FP32 = PrefillWorkload("tiny-fp32 T=6 H=4 KV=2 hd=8", 1, 6, 4, 2, 8, F32, 0, 10000.0)
+SMALL_BF16 = PrefillWorkload("small-bf16 B=1 T=512 H=8 KV=2 hd=64", 1, 512, 8, 2, 64, BF16, 2, 10000.0)
+LLAMA3_8B = PrefillWorkload("llama3-8b-prefill B=4 T=4096 H=32 KV=8 hd=128 rope=5e5",
+                            4, 4096, 32, 8, 128, BF16, 3, 500000.0)
+ALIBI_MHA = PrefillWorkload("alibi-mha-prefill B=8 T=2048 H=16 KV=16 hd=128",
+                            8, 2048, 16, 16, 128, BF16, 4, 0.0, alibi=1)
+KV_DECODE = DecodeWorkload("kv-decode B=64 len~U[512,8192] H=32 KV=8 hd=128",
+                           64, 32, 8, 128, 512, 8192, 5, 5, 10000.0)
+
+PREFILL_WORKLOADS = {"tiny": TINY_FP32, "small": SMALL_BF16, "llama3": LLAMA3_8B, "alibi": ALIBI_MHA}
+
+
+def lab_instance():
+    """The seeded instance of the attention lab page: x, Wq, Wk, Wv, Wo (fp64).
+
+    T=6 tokens, width d=32, H=4 query heads, KV=2 key/value heads, hd=8.
+    """
+    rng = np.random.default_rng(0)
+    T, d, H, KV = 6, 32, 4, 2
+    hd = d // H
+    x = rng.normal(size=(T, d))
+    Wq = rng.normal(size=(d, H * hd)) / np.sqrt(d)
+    Wk = rng.normal(size=(d, KV * hd)) / np.sqrt(d)
+    Wv = rng.normal(size=(d, KV * hd)) / np.sqrt(d)
+    Wo = rng.normal(size=(H * hd, d)) / np.sqrt(d)
+    return x, Wq, Wk, Wv, Wo
+
+
+def split_heads(y: np.ndarray, heads: int) -> np.ndarray:
+    """[T, heads*hd] -> [1, heads, T, hd] (a reshape; no arithmetic)."""
+    T = y.shape[0]
+    return np.ascontiguousarray(y.reshape(T, heads, -1).transpose(1, 0, 2)[None])
+
+
+def tiny_qkv(x: np.ndarray | None = None):
+    """Q/K/V of the lab instance as fp32 arrays [1,H,T,hd], [1,KV,T,hd] (host projections)."""
+    x0, Wq, Wk, Wv, _ = lab_instance()
+    if x is None:
+        x = x0
+    q = split_heads(x @ Wq, 4).astype(np.float32)
+    k = split_heads(x @ Wk, 2).astype(np.float32)
+    v = split_heads(x @ Wv, 2).astype(np.float32)
+    return q, k, v
+
+
+def normal_bf16(gen: torch.Generator, shape) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def normal_f32(gen: torch.Generator, shape) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32)
+
+
+def prefill_inputs(w: PrefillWorkload, *, B: int | None = None, T: int | None = None):
+    """Host tensors q [B,H,T,hd], k, v [B,KV,T,hd] for a prefill workload.
+
+    ``B``/``T`` override the sizes (same seed and draw order) for scaled-down cases.
+    """
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    if w is TINY_FP32 and B == 1 and T == 6:
+        q, k, v = tiny_qkv()
+        return torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)
+    g = torch.Generator().manual_seed(w.seed)
+    draw = normal_bf16 if w.dtype == BF16 else normal_f32
+    q = draw(g, (B, w.H, T, w.hd))
+    k = draw(g, (B, w.KV, T, w.hd))
+    v = draw(g, (B, w.KV, T, w.hd))
+    return q, k, v
+
+
+def random_prefill(seed: int, B: int, T: int, H: int, KV: int, hd: int, dtype: str = BF16, scale: float = 1.0):
+    """Generic seeded q/k/v for parity sweeps (same draw order as the workloads)."""
+    g = torch.Generator().manual_seed(seed)
+    draw = normal_bf16 if dtype == BF16 else normal_f32
+    q = draw(g, (B, H, T, hd))
+    k = draw(g, (B, KV, T, hd))
+    v = draw(g, (B, KV, T, hd))
+    if scale != 1.0:
+        q = (q.float() * scale).to(q.dtype)
+        k = (k.float() * scale).to(k.dtype)
+    return q, k, v
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor        # [B, H, hd]
+    k_new: torch.Tensor    # [B, KV, hd]
+    v_new: torch.Tensor    # [B, KV, hd]
+    k_cache: torch.Tensor  # [B, KV, Lmax, hd] (valid prefix per sequence; rest zero)
+    v_cache: torch.Tensor
+    lens: np.ndarray       # [B] int32
+    extra: dict = field(default_factory=dict)
+
+
+def decode_inputs(w: DecodeWorkload, *, B: int | None = None, lens: np.ndarray | None = None,
+                  lmax: int | None = None, device: str | torch.device = "cpu") -> DecodeInputs:
+    """Seeded decode inputs. The cache is filled sequence by sequence (draw order b = 0..B-1)
+    directly into a tensor on ``device`` so that the full-size cache never exists twice."""
+    if lens is None:
+        lens = w.lengths()
+    lens = np.asarray(lens, dtype=np.int32)
+    if B is not None:
+        lens = lens[:B]
+    B = len(lens)
+    Lmax = int(lens.max()) + 1 if lmax is None else lmax
+    g = torch.Generator().manual_seed(w.seed)
+    draw = normal_bf16 if w.dtype == BF16 else normal_f32
+    q = draw(g, (B, w.H, w.hd))
+    k_new = draw(g, (B, w.KV, w.hd))
+    v_new = draw(g, (B, w.KV, w.hd))
+    tdt = torch.bfloat16 if w.dtype == BF16 else torch.float32
+    k_cache = torch.zeros(B, w.KV, Lmax, w.hd, dtype=tdt, device=device)
+    v_cache = torch.zeros(B, w.KV, Lmax, w.hd, dtype=tdt, device=device)
+    for b in range(B):
+        L = int(lens[b])
+        k_cache[b, :, :L] = draw(g, (w.KV, L, w.hd)).to(device)
+        v_cache[b, :, :L] = draw(g, (w.KV, L, w.hd)).to(device)
+    return DecodeInputs(q, k_new, v_new, k_cache, v_cache, lens)
