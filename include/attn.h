@@ -1,0 +1,152 @@
+/*
+ * attn.h — C ABI of libattn.so: causal grouped-query attention forward with
+ * rotary embeddings and ALiBi for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (fixed by the source pages):
+ *   out[b,h,i] = sum_j softmax_j( <R(p_i) q[b,h,i], R(p_j) k[b,g,j]> / sqrt(hd)
+ *                                 - slope_h * |i - j| ) * v[b,g,j]
+ *   with g = h / (H / KV) (grouped-query sharing, consecutive groups),
+ *   j <= i when causal, R(p) the interleaved-pair rotary rotation at position p
+ *   (pair (2m, 2m+1) turned by p * base^(-2m/hd)), V never rotated.
+ *   Sources: "Building a Transformer from Scratch: Attention, Architecture, and
+ *   Memory" (Part 1, scaled dot-product equation; Part 3, the online-softmax
+ *   recurrences), "Write attention from scratch" (the lab listing: rope with a
+ *   position offset, np.repeat grouping, lower-triangular mask), "Building a
+ *   Multi-Head Self-Attention Block with RoPE and ALiBi from Scratch" (Step 3:
+ *   ALiBi bias as slope times distance, added after the 1/sqrt(d_k) scaling),
+ *   "Building Grouped-Query Attention with RoPE and Flash Attention from
+ *   Scratch" (Step 3: tiled online softmax; roadmap: bf16 inputs with fp32
+ *   softmax statistics and accumulation; cache written by position).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never frees, retains or allocates memory and never synchronises.
+ *   - Tensors are dense, row-major, with the shapes stated per function.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; a return of ATTN_OK means "enqueued".
+ *   - Every argument is validated before any HIP call; on failure nothing is
+ *     enqueued, the status code says why and attn_last_error() gives detail.
+ *   - No C++ exception crosses this boundary. Functions are thread-safe; the
+ *     error text is per calling thread.
+ *   - dtype / out_dtype: ATTN_DTYPE_F32 or ATTN_DTYPE_BF16. Softmax statistics
+ *     and accumulation are always fp32; bf16 outputs are rounded to nearest
+ *     even.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* Status codes. */
+#define ATTN_OK 0
+#define ATTN_ERR_NULL 1        /* a required pointer is NULL */
+#define ATTN_ERR_SHAPE 2       /* non-positive size, H % KV != 0, odd hd, negative pos0, size overflow */
+#define ATTN_ERR_UNSUPPORTED 3 /* hd not in {8,16,32,64,128}, unknown dtype / flag value */
+#define ATTN_ERR_ALIGN 4       /* q/k/v/out/cache pointers not 16-byte aligned, workspace not 256-byte aligned */
+#define ATTN_ERR_WORKSPACE 5   /* workspace missing or smaller than the *_workspace_bytes() figure */
+#define ATTN_ERR_HIP 6         /* a HIP launch failed (no device, invalid stream, ...) */
+
+/* Element types. */
+#define ATTN_DTYPE_F32 0
+#define ATTN_DTYPE_BF16 1
+
+/* ALiBi slope families (the bias itself is -slope_h * |i - j|). */
+#define ATTN_ALIBI_NONE 0
+#define ATTN_ALIBI_GEOMETRIC 1 /* slope_h = 2^(-8(h+1)/H), h = 0..H-1 */
+#define ATTN_ALIBI_PAGE1 2     /* slope_h = 2^(-2(h+1)/H): the heuristic printed in Step 1 of the
+                                  multi-head RoPE+ALiBi page */
+
+/* ABI version of the loaded library (ATTN_ABI_VERSION it was built with). */
+int attn_abi_version(void);
+
+/* Static, never-NULL name of a status code ("ATTN_OK", ..., "unknown status"). */
+const char* attn_status_str(int status);
+
+/* Detail of the last non-OK status returned to this thread ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * Bytes of device workspace attn_prefill_fwd needs: the rotated keys,
+ * B*KV*T*hd elements of `dtype`, when rope_base != 0; 0 without rotary
+ * embedding. Returns 0 for invalid sizes (the forward call reports why).
+ */
+size_t attn_prefill_workspace_bytes(int B, int T, int KV, int hd, int dtype, double rope_base);
+
+/*
+ * Prefill / full-sequence attention forward ("Building Grouped-Query Attention
+ * with RoPE and Flash Attention from Scratch", Step 3, with the causal mask of
+ * "Write attention from scratch" and ALiBi of the multi-head page, Step 3).
+ *
+ *   q    [B, H,  T, hd]  dtype, before rotation
+ *   k    [B, KV, T, hd]  dtype, before rotation
+ *   v    [B, KV, T, hd]  dtype
+ *   out  [B, H,  T, hd]  out_dtype (written)
+ *   lse  [B, H,  T]      fp32 natural-log log-sum-exp of each row's scaled,
+ *                        biased scores (written); may be NULL
+ *   Token t of every sequence sits at position pos0 + t (for the rotation);
+ *   the causal test and the ALiBi distance use token indices.
+ *   rope_base: rotary base (10000, 500000, ...); 0 disables the rotation.
+ *   causal: 1 keeps keys j <= i, 0 attends all keys.
+ *   alibi: ATTN_ALIBI_* (0 = none).
+ *   Scale is fixed at 1/sqrt(hd).
+ *   workspace: device scratch of at least attn_prefill_workspace_bytes(...)
+ *   bytes (may be NULL when that figure is 0); its contents are clobbered.
+ *
+ * q, k, v, out and workspace must not overlap. Runs the MFMA kernel for bf16
+ * with hd in {64,128} and H/KV dividing 8, and a vector-ALU kernel otherwise.
+ */
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int T, int H, int KV, int hd, int pos0, double rope_base,
+                     int causal, int alibi, int dtype, int out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_fwd needs for its split-KV partials
+ * (fp32 partial outputs and their max / denominator per split). 0 for invalid
+ * sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax);
+
+/*
+ * One KV-cache decode step for B sequences ("Write attention from scratch",
+ * Exercise 2: the incremental result equals the full computation; "Building
+ * Grouped-Query Attention ...", roadmap: a pre-allocated cache written by
+ * position; "Building a Transformer from Scratch", Part 3: KV caching).
+ *
+ *   q          [B, H,  hd]        dtype, the new token's query before rotation
+ *   k_new      [B, KV, hd]        dtype, the new token's key before rotation
+ *   v_new      [B, KV, hd]        dtype
+ *   k_cache    [B, KV, Lmax, hd]  dtype, rotated keys at slots 0..L-1 (read);
+ *                                 slot L receives R(L) k_new (written)
+ *   v_cache    [B, KV, Lmax, hd]  dtype, values at slots 0..L-1 (read);
+ *                                 slot L receives v_new (written)
+ *   cache_lens [B] int32 device   L = cache_lens[b] >= 0 tokens already cached;
+ *                                 must satisfy L < Lmax (not checked on the host,
+ *                                 which does not read device memory; a device
+ *                                 side clamp keeps accesses in bounds)
+ *   out        [B, H, hd]         out_dtype (written)
+ *   lse        [B, H]             fp32 (written); may be NULL
+ *   The new token sits at position L: its query and key are rotated at L and
+ *   the query attends slots 0..L inclusive (ALiBi distance L - j).
+ *   workspace: at least attn_decode_workspace_bytes(B, H, KV, hd, Lmax) bytes.
+ *
+ * Runs, in stream order: the cache append, the split-KV partial kernel, and
+ * the log-sum-exp merge of the partials.
+ */
+int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* cache_lens, void* out, float* lse,
+                    int B, int H, int KV, int hd, int Lmax, double rope_base, int alibi,
+                    int dtype, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: symbols, status strings, argument validation.
+
+Every validation error must come back before any HIP call, so these tests pass
+fake (never dereferenced) device addresses.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_attention_02_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="libattn.so not built")
+
+FAKE = 0x10000  # 64 KiB: 256-byte aligned, never dereferenced by a failing call
+FAKE2 = 0x20000
+FAKE3 = 0x30000
+FAKE4 = 0x40000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert header_functions() == sorted(bd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert bd.attn_abi_version() == 1
+    names = {c: bd.attn_status_str(c) for c in range(7)}
+    assert names == {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+                     4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP"}
+    assert bd.attn_status_str(99) == "unknown status"
+
+
+def _prefill(**kw):
+    args = dict(q=FAKE, k=FAKE2, v=FAKE3, out=FAKE4, lse=None, B=1, T=16, H=4, KV=2, hd=64, pos0=0,
+                rope_base=10000.0, causal=1, alibi=0, dtype=bd.ATTN_DTYPE_BF16, out_dtype=bd.ATTN_DTYPE_F32,
+                workspace=0x100000, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return bd.attn_prefill_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), bd.ATTN_ERR_NULL),
+    (dict(out=None), bd.ATTN_ERR_NULL),
+    (dict(B=0), bd.ATTN_ERR_SHAPE),
+    (dict(T=-1), bd.ATTN_ERR_SHAPE),
+    (dict(H=6, KV=4), bd.ATTN_ERR_SHAPE),
+    (dict(hd=7), bd.ATTN_ERR_SHAPE),
+    (dict(hd=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(hd=256), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(pos0=-1), bd.ATTN_ERR_SHAPE),
+    (dict(dtype=7), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(out_dtype=2), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(alibi=3), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(causal=2), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(rope_base=-5.0), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(rope_base=float("nan")), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 2), bd.ATTN_ERR_ALIGN),
+    (dict(out=FAKE4 + 8), bd.ATTN_ERR_ALIGN),
+    (dict(lse=FAKE + 1), bd.ATTN_ERR_ALIGN),
+    (dict(workspace=None), bd.ATTN_ERR_WORKSPACE),
+    (dict(workspace_bytes=100), bd.ATTN_ERR_WORKSPACE),
+    (dict(workspace=0x100010), bd.ATTN_ERR_ALIGN),
+])
+def test_prefill_validation(kw, code):
+    st = _prefill(**kw)
+    assert st == code, (st, bd.attn_last_error())
+    assert bd.attn_last_error() != ""
+
+
+def test_prefill_workspace_sizes():
+    assert bd.attn_prefill_workspace_bytes(4, 4096, 8, 128, bd.ATTN_DTYPE_BF16, 500000.0) == 4 * 8 * 4096 * 128 * 2
+    assert bd.attn_prefill_workspace_bytes(1, 6, 2, 8, bd.ATTN_DTYPE_F32, 10000.0) == 6 * 2 * 8 * 4
+    assert bd.attn_prefill_workspace_bytes(8, 2048, 16, 128, bd.ATTN_DTYPE_BF16, 0.0) == 0
+    assert bd.attn_prefill_workspace_bytes(0, 1, 1, 8, bd.ATTN_DTYPE_BF16, 1e4) == 0
+
+
+def test_no_rope_needs_no_workspace_check():
+    # rope off: workspace may be NULL; validation passes to the launch stage.
+    if _gpu_present():
+        pytest.skip("would launch on a real device")
+    st = _prefill(rope_base=0.0, workspace=None, workspace_bytes=0)
+    assert st == bd.ATTN_ERR_HIP
+
+
+def _decode(**kw):
+    args = dict(q=FAKE, k_new=FAKE2, v_new=FAKE3, k_cache=FAKE4, v_cache=0x50000, cache_lens=0x60000,
+                out=0x70000, lse=None, B=2, H=8, KV=2, hd=128, Lmax=1000, rope_base=10000.0, alibi=0,
+                dtype=bd.ATTN_DTYPE_BF16, out_dtype=bd.ATTN_DTYPE_F32, workspace=0x100000,
+                workspace_bytes=1 << 24, stream=None)
+    args.update(kw)
+    return bd.attn_decode_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cache_lens=None), bd.ATTN_ERR_NULL),
+    (dict(k_cache=None), bd.ATTN_ERR_NULL),
+    (dict(Lmax=0), bd.ATTN_ERR_SHAPE),
+    (dict(H=8, KV=3), bd.ATTN_ERR_SHAPE),
+    (dict(hd=48), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(alibi=-1), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(k_cache=FAKE4 + 4), bd.ATTN_ERR_ALIGN),
+    (dict(cache_lens=0x60002), bd.ATTN_ERR_ALIGN),
+    (dict(workspace=None), bd.ATTN_ERR_WORKSPACE),
+    (dict(workspace_bytes=64), bd.ATTN_ERR_WORKSPACE),
+])
+def test_decode_validation(kw, code):
+    st = _decode(**kw)
+    assert st == code, (st, bd.attn_last_error())
+
+
+def test_decode_workspace_size():
+    n = bd.attn_decode_workspace_bytes(64, 32, 8, 128, 8193)
+    nsplit = -(-8193 // 256)
+    assert n >= 64 * 32 * nsplit * (128 * 4 + 8) and n % 256 == 0
+    assert bd.attn_decode_workspace_bytes(0, 32, 8, 128, 8193) == 0
+
+
+def _gpu_present():
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+def test_launch_without_a_device_reports_hip_error():
+    if _gpu_present():
+        pytest.skip("a device is present")
+    st = _prefill()
+    assert st == bd.ATTN_ERR_HIP
+    assert "launch" in bd.attn_last_error()

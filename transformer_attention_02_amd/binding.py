@@ -1,0 +1,212 @@
+"""ctypes binding of libattn.so (argument marshalling only).
+
+The raw functions keep the C names and signatures of ``include/attn.h``
+(pointers are Python ints). :func:`prefill` and :func:`decode` accept torch
+tensors already on the GPU, allocate the outputs and workspace with torch (the
+memory and streams are torch's; every step of the computation runs in the
+library's HIP kernels) and raise :class:`AttnError` on a non-OK status.
+
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULL = 1
+ATTN_ERR_SHAPE = 2
+ATTN_ERR_UNSUPPORTED = 3
+ATTN_ERR_ALIGN = 4
+ATTN_ERR_WORKSPACE = 5
+ATTN_ERR_HIP = 6
+
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+
+ATTN_ALIBI_NONE = 0
+ATTN_ALIBI_GEOMETRIC = 1
+ATTN_ALIBI_PAGE1 = 2
+
+EXPORTS = (
+    "attn_abi_version",
+    "attn_status_str",
+    "attn_last_error",
+    "attn_prefill_workspace_bytes",
+    "attn_prefill_fwd",
+    "attn_decode_workspace_bytes",
+    "attn_decode_fwd",
+)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_D = ctypes.c_double
+_S = ctypes.c_size_t
+
+_SIGS = {
+    "attn_abi_version": (_I, []),
+    "attn_status_str": (ctypes.c_char_p, [_I]),
+    "attn_last_error": (ctypes.c_char_p, []),
+    "attn_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _D]),
+    "attn_prefill_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I, _I, _I, _P, _S, _P]),
+    "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "attn_decode_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I, _P, _S, _P]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_str(status)}: {detail}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Open libattn.so (once) and declare its signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is not built; run `python -m transformer_attention_02_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def attn_abi_version() -> int:
+    return load().attn_abi_version()
+
+
+def attn_status_str(status: int) -> str:
+    return load().attn_status_str(status).decode()
+
+
+status_str = attn_status_str
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def attn_prefill_workspace_bytes(B, T, KV, hd, dtype, rope_base) -> int:
+    return load().attn_prefill_workspace_bytes(B, T, KV, hd, dtype, float(rope_base))
+
+
+def attn_prefill_fwd(q, k, v, out, lse, B, T, H, KV, hd, pos0, rope_base, causal, alibi, dtype, out_dtype,
+                     workspace, workspace_bytes, stream) -> int:
+    return load().attn_prefill_fwd(q, k, v, out, lse, B, T, H, KV, hd, pos0, float(rope_base), causal, alibi,
+                                   dtype, out_dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_workspace_bytes(B, H, KV, hd, Lmax) -> int:
+    return load().attn_decode_workspace_bytes(B, H, KV, hd, Lmax)
+
+
+def attn_decode_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base, alibi,
+                    dtype, out_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().attn_decode_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax,
+                                  float(rope_base), alibi, dtype, out_dtype, workspace, workspace_bytes, stream)
+
+
+# --------------------------------------------------------------- torch helpers
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ATTN_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _stream_ptr(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def prefill_workspace(B, T, KV, hd, dtype_code, rope_base, device):
+    import torch
+
+    n = attn_prefill_workspace_bytes(B, T, KV, hd, dtype_code, rope_base)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
+
+
+def prefill(q, k, v, *, pos0=0, rope_base=10000.0, causal=True, alibi=ATTN_ALIBI_NONE, out_dtype=None,
+            want_lse=True, out=None, lse=None, workspace=None, stream=None):
+    """Run attn_prefill_fwd on torch tensors q [B,H,T,hd], k/v [B,KV,T,hd] (same dtype, contiguous, on GPU).
+
+    Returns (out, lse). ``out_dtype`` defaults to fp32.
+    """
+    import torch
+
+    assert q.is_cuda and k.is_cuda and v.is_cuda, "tensors must be on the GPU"
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    B, H, T, hd = q.shape
+    KV = k.shape[1]
+    dt = _dtype_code(q)
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(B, H, T, hd, dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace, nbytes = prefill_workspace(B, T, KV, hd, dt, rope_base, q.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    st = attn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if lse is not None else None, B, T, H, KV, hd, pos0, rope_base,
+                          int(causal), alibi, dt, _dtype_code(out), workspace.data_ptr(), nbytes,
+                          _stream_ptr(stream))
+    _check(st)
+    return out, lse
+
+
+def decode_workspace(B, H, KV, hd, Lmax, device):
+    import torch
+
+    n = attn_decode_workspace_bytes(B, H, KV, hd, Lmax)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
+
+
+def decode(q, k_new, v_new, k_cache, v_cache, cache_lens, *, rope_base=10000.0, alibi=ATTN_ALIBI_NONE,
+           out_dtype=None, want_lse=True, out=None, lse=None, workspace=None, stream=None):
+    """Run attn_decode_fwd on GPU torch tensors (see include/attn.h for shapes). Returns (out, lse)."""
+    import torch
+
+    B, H, hd = q.shape
+    KV, Lmax = k_cache.shape[1], k_cache.shape[2]
+    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
+    dt = _dtype_code(q)
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(B, H, hd, dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace, nbytes = decode_workspace(B, H, KV, hd, Lmax, q.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    st = attn_decode_fwd(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                         cache_lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                         B, H, KV, hd, Lmax, rope_base, alibi, dt, _dtype_code(out), workspace.data_ptr(), nbytes,
+                         _stream_ptr(stream))
+    _check(st)
+    return out, lse

@@ -1,0 +1,221 @@
+// C ABI of libattn.so: argument validation, workspace sizing and dispatch.
+// Every check runs before the first HIP call; nothing here allocates, frees or
+// synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+using namespace attn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool supported_hd(int hd) { return hd == 8 || hd == 16 || hd == 32 || hd == 64 || hd == 128; }
+
+size_t elem_bytes(int dtype) { return dtype == ATTN_DTYPE_BF16 ? 2 : 4; }
+
+// theta_i / (2 pi) = base^(-2i/hd) / (2 pi) in fp64.
+RopeFreqs make_freqs(int hd, double base) {
+  RopeFreqs f;
+  memset(&f, 0, sizeof(f));
+  if (base != 0.0) {
+    for (int i = 0; i < hd / 2; ++i) f.rev[i] = pow(base, -2.0 * i / hd) / (2.0 * M_PI);
+  }
+  return f;
+}
+
+int check_common(int dtype, int out_dtype, int alibi, double rope_base, int hd) {
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (out_dtype != ATTN_DTYPE_F32 && out_dtype != ATTN_DTYPE_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if (alibi < ATTN_ALIBI_NONE || alibi > ATTN_ALIBI_PAGE1) return fail(ATTN_ERR_UNSUPPORTED, "alibi %d", alibi);
+  if (!(rope_base >= 0.0) || !isfinite(rope_base) || (rope_base > 0.0 && rope_base <= 1.0))
+    return fail(ATTN_ERR_UNSUPPORTED, "rope_base %g (0 disables, otherwise > 1)", rope_base);
+  if (hd <= 0 || hd % 2) return fail(ATTN_ERR_SHAPE, "head dim %d must be positive and even", hd);
+  if (!supported_hd(hd)) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d not in {8,16,32,64,128}", hd);
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr long long kMaxElems = 1LL << 40;
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t attn_prefill_workspace_bytes(int B, int T, int KV, int hd, int dtype, double rope_base) {
+  if (B <= 0 || T <= 0 || KV <= 0 || hd <= 0 || rope_base == 0.0) return 0;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return 0;
+  const long long n = (long long)B * KV * T * hd;
+  if (n > kMaxElems) return 0;
+  return (size_t)n * elem_bytes(dtype);
+}
+
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int T, int H,
+                     int KV, int hd, int pos0, double rope_base, int causal, int alibi, int dtype, int out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out) return fail(ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
+  if (B <= 0 || T <= 0 || H <= 0 || KV <= 0)
+    return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d KV=%d)", B, T, H, KV);
+  if (H % KV) return fail(ATTN_ERR_SHAPE, "H=%d is not a multiple of KV=%d", H, KV);
+  if (pos0 < 0 || (long long)pos0 + T > 0x7fffffffLL) return fail(ATTN_ERR_SHAPE, "pos0=%d out of range", pos0);
+  if (H > 65535 || B > 65535) return fail(ATTN_ERR_SHAPE, "H and B must be <= 65535");
+  if (int c = check_common(dtype, out_dtype, alibi, rope_base, hd)) return c;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_UNSUPPORTED, "causal %d", causal);
+  if ((long long)B * H * T * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "tensor too large");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(ATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(ATTN_ERR_ALIGN, "lse must be 4-byte aligned");
+  const size_t need = attn_prefill_workspace_bytes(B, T, KV, hd, dtype, rope_base);
+  if (need) {
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+
+  const int bf16 = dtype == ATTN_DTYPE_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.KV = KV;
+  a.hd = hd;
+  a.group = H / KV;
+  a.pos0 = pos0;
+  a.causal = causal;
+  a.rope = rope_base != 0.0;
+  a.alibi = alibi;
+  a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  a.freqs = make_freqs(hd, rope_base);
+
+  if (a.rope) {
+    RopeKArgs r;
+    r.k = k;
+    r.kr = workspace;
+    r.rows = (long)B * KV * T;
+    r.T = T;
+    r.hd = hd;
+    r.pos0 = pos0;
+    r.freqs = a.freqs;
+    if (int c = hip_status(launch_rope_k(r, bf16, s), "rope_k launch")) return c;
+    a.k = workspace;
+  }
+  if (prefill_mfma_supported(a, bf16)) return hip_status(launch_prefill_mfma(a, s), "prefill_mfma launch");
+  return hip_status(launch_prefill_valu(a, bf16, s), "prefill_valu launch");
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax) {
+  if (B <= 0 || H <= 0 || KV <= 0 || hd <= 0 || Lmax <= 0) return 0;
+  const long long nsplit = (Lmax + kDecodeSplit - 1) / kDecodeSplit;
+  const long long rows = (long long)B * H * nsplit;
+  const long long bytes = rows * hd * 4 + rows * 8;
+  return (size_t)((bytes + 255) / 256 * 256);
+}
+
+int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
+                    double rope_base, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !out)
+    return fail(ATTN_ERR_NULL, "q, k_new, v_new, k_cache, v_cache, cache_lens and out must be non-NULL");
+  if (B <= 0 || H <= 0 || KV <= 0 || Lmax <= 0)
+    return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d H=%d KV=%d Lmax=%d)", B, H, KV, Lmax);
+  if (H % KV) return fail(ATTN_ERR_SHAPE, "H=%d is not a multiple of KV=%d", H, KV);
+  if (H > 65535 || B > 65535 || KV > 65535) return fail(ATTN_ERR_SHAPE, "H, KV and B must be <= 65535");
+  if (int c = check_common(dtype, out_dtype, alibi, rope_base, hd)) return c;
+  if ((long long)B * KV * Lmax * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "cache too large");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(cache_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(ATTN_ERR_ALIGN, "cache_lens and lse must be 4-byte aligned");
+  const size_t need = attn_decode_workspace_bytes(B, H, KV, hd, Lmax);
+  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.lens = cache_lens;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.KV = KV;
+  a.hd = hd;
+  a.group = H / KV;
+  a.Lmax = Lmax;
+  a.nsplit = (Lmax + kDecodeSplit - 1) / kDecodeSplit;
+  const long long rows = (long long)B * H * a.nsplit;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(workspace) + rows * hd * 4);
+  a.rope = rope_base != 0.0;
+  a.alibi = alibi;
+  a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  a.freqs = make_freqs(hd, rope_base);
+  return hip_status(launch_decode(a, dtype == ATTN_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+}  // extern "C"
