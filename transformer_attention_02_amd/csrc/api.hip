@@ -39,12 +39,12 @@ bool supported_hd(int hd) { return hd == 8 || hd == 16 || hd == 32 || hd == 64 |
 
 size_t elem_bytes(int dtype) { return dtype == ATTN_DTYPE_BF16 ? 2 : 4; }
 
-// theta_i / (2 pi) = base^(-2i/hd) / (2 pi) in fp64.
+// 4 theta_i / (2 pi) = base^(-2i/hd) * 2 / pi in fp64: quarter turns per position.
 RopeFreqs make_freqs(int hd, double base) {
   RopeFreqs f;
   memset(&f, 0, sizeof(f));
   if (base != 0.0) {
-    for (int i = 0; i < hd / 2; ++i) f.rev[i] = pow(base, -2.0 * i / hd) / (2.0 * M_PI);
+    for (int i = 0; i < hd / 2; ++i) f.rev[i] = pow(base, -2.0 * i / hd) * (2.0 / M_PI);
   }
   return f;
 }

@@ -11,7 +11,8 @@ namespace attn {
 constexpr int kMaxHeadDim = 128;
 constexpr int kDecodeSplit = 256;  // keys per split-KV partial in decode
 
-// theta_i / (2 pi) in fp64 for i = 0 .. hd/2-1, theta_i = base^(-2i/hd).
+// 4 theta_i / (2 pi) in fp64 (quarter turns per position) for i = 0 .. hd/2-1,
+// theta_i = base^(-2i/hd).
 // Passed by value so the kernels need no table in device memory.
 struct RopeFreqs {
   double rev[kMaxHeadDim / 2];
@@ -79,14 +80,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
-// cos/sin of the rotary angle pos * theta, where rev = theta / (2 pi) in fp64.
-// The angle is reduced to [-pi, pi] in fp64 before the fp32 sincos, so the
-// result is accurate to fp32 rounding for any position.
-__device__ __forceinline__ void rope_cos_sin(int pos, double rev, float& c, float& s) {
-  double a = (double)pos * rev;
-  a -= rint(a);
-  float r = (float)(a * 6.283185307179586476925286766559);
-  sincosf(r, &s, &c);
+// cos/sin of the rotary angle pos * theta, with q4 = 4 * theta / (2 pi) in fp64
+// (the angle in quarter turns per position). The angle is reduced in fp64 to a
+// quadrant k and a remainder f in [-pi/4, pi/4]; sin f and cos f are the Taylor
+// series to degree 9 and 8 (truncation below 3e-8 on that interval), and the
+// quadrant rotates the pair. Accurate to fp32 rounding for any position.
+__device__ __forceinline__ void rope_cos_sin(int pos, double q4, float& c, float& s) {
+  const double x = (double)pos * q4;
+  const double k = rint(x);
+  const float f = (float)((x - k) * 1.5707963267948966);
+  const float f2 = f * f;
+  const float sf = f * fmaf(f2, fmaf(f2, fmaf(f2, fmaf(f2, 2.7557319223985893e-6f, -1.9841269841269841e-4f),
+                                                 8.3333333333333333e-3f), -1.6666666666666667e-1f), 1.0f);
+  const float cf = fmaf(f2, fmaf(f2, fmaf(f2, fmaf(f2, 2.4801587301587302e-5f, -1.3888888888888889e-3f),
+                                          4.1666666666666667e-2f), -0.5f), 1.0f);
+  const int q = (int)((long long)k & 3);
+  const float s1 = (q & 1) ? cf : sf;
+  const float c1 = (q & 1) ? sf : cf;
+  s = (q & 2) ? -s1 : s1;
+  c = ((q + 1) & 2) ? -c1 : c1;
 }
 
 // ALiBi slope of head h out of H for the two slope families, in fp32.

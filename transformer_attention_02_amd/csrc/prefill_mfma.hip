@@ -1,10 +1,355 @@
-// bf16 MFMA prefill kernel (gfx950). Placeholder until the MFMA kernel lands.
+// bf16 matrix-core prefill kernel for gfx950 (CDNA4).
+//
+// Computes the tiled online-softmax attention forward ("Building Grouped-Query
+// Attention with RoPE and Flash Attention from Scratch", Step 3; recurrences of
+// "Building a Transformer from Scratch", Part 3) with bf16 operands and fp32
+// softmax statistics and accumulation (that page's mixed-precision roadmap item).
+//
+// Work decomposition
+//   * A workgroup is 4 waves. It owns one block of query rows for up to 4 query
+//     heads that share one key/value head (grouped-query packing), so every
+//     K/V tile staged in LDS serves all of them.
+//   * A wave owns 32 query rows of one head and computes S^T = K Q^T with
+//     v_mfma_f32_32x32x16_bf16. In the 32x32 accumulator a lane holds one
+//     query (column) and 16 keys (rows), so the row max and row sum are
+//     in-lane reductions plus one exchange between the two half-waves.
+//   * The key rows fed to the S^T contraction are permuted (bits 2 and 3 of
+//     the row index swapped) so that accumulator registers 8u..8u+7 of a lane
+//     hold 8 consecutive keys: the probabilities then feed O^T = V^T P^T as the
+//     B operand straight from registers (rounded to bf16), and V^T is read from
+//     LDS as 16-byte rows.
+//   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
+//     j+1 are in flight while tile j is computed. V is transposed on its way
+//     into LDS. Both tiles use XOR swizzles so the MFMA operand reads are free
+//     of bank conflicts.
+//   * Causal: tiles past the diagonal are never loaded; a wave skips tiles that
+//     are entirely above its rows; only tiles crossing the diagonal (or the
+//     ragged end of the sequence) are masked.
+//   * Rotary embedding of Q is fused into the Q load (fp32 rotation, rounded to
+//     bf16); K arrives already rotated (a pre-pass writes it once).
+//   * Workgroups are numbered so that every workgroup touching one key/value
+//     head lands on the same XCD (its L2 keeps that head's K/V), heaviest
+//     causal blocks first.
 #include "attn_internal.h"
 
 namespace attn {
 
-bool prefill_mfma_supported(const PrefillArgs&, int) { return false; }
+namespace {
 
-hipError_t launch_prefill_mfma(const PrefillArgs&, hipStream_t) { return hipErrorInvalidDeviceFunction; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BN = 64;  // keys per tile
+constexpr int NW = 4;   // waves per workgroup
+constexpr int NT = NW * 64;
+
+template <int HD>
+struct Cfg {
+  static constexpr int KCH = HD / 8;               // 16-byte chunks per key row
+  static constexpr int K_BYTES = BN * HD * 2;      // K tile, row-major [key][hd]
+  static constexpr int V_BYTES = HD * BN * 2;      // V^T tile, [hd][key]
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int K_LOADS = BN * KCH / NT;    // 16-byte K loads per thread
+  static constexpr int V_UNITS = (BN / 4) * KCH;   // (4 keys x 8 dims) V units
+};
+
+struct GridMap {
+  int hpw;       // heads per workgroup (1, 2 or 4)
+  int hchunks;   // group / hpw
+  int bm;        // query rows per head per workgroup = 32 * (4 / hpw)
+  int nqb;       // query blocks
+  int units;     // B * KV * hchunks
+  int xcd_aware;
+};
+
+// Byte offset of 16-byte chunk `c` of key row `r` in the K tile (XOR swizzle).
+template <int HD>
+__device__ __forceinline__ int k_off(int r, int c) {
+  if constexpr (HD == 128) {
+    return r * 256 + ((c ^ (r & 15)) << 4);
+  } else {
+    return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+  }
+}
+
+// Byte offset of 16-byte chunk `c` (8 keys) of row `d` of the V^T tile.
+__device__ __forceinline__ int v_off(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
+
+// Swap bits 2 and 3 of a row index in [0, 32).
+__device__ __forceinline__ int perm_row(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Component i (a compile-time constant after unrolling) of a uint4, without taking its address.
+__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
+
+// Registers holding one K/V tile between its global load and its LDS store.
+// Thread t loads K chunks e = t + 256 i (row e / KCH, chunk e % KCH) and, if it
+// owns a V unit, 4 consecutive keys x 8 dims that it writes transposed.
+template <int HD>
+struct Stage {
+  using C = Cfg<HD>;
+  uint4 k[C::K_LOADS];
+  uint4 v0, v1, v2, v3;
+
+  __device__ __forceinline__ void load(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, int tid, int vkg,
+                                       int vch, bool v_thread) {
+#pragma unroll
+    for (int i = 0; i < C::K_LOADS; ++i) {
+      const int e = tid + NT * i;
+      const int r = e / C::KCH, c = e % C::KCH;
+      const int key = kt * BN + r;
+      k[i] = key < T ? *reinterpret_cast<const uint4*>(Kg + (long)key * HD + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if (v_thread) {
+      const int key = kt * BN + 4 * vkg;
+      const uint16_t* p = Vg + (long)key * HD + vch * 8;
+      v0 = key + 0 < T ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+      v1 = key + 1 < T ? *reinterpret_cast<const uint4*>(p + HD) : make_uint4(0, 0, 0, 0);
+      v2 = key + 2 < T ? *reinterpret_cast<const uint4*>(p + 2 * HD) : make_uint4(0, 0, 0, 0);
+      v3 = key + 3 < T ? *reinterpret_cast<const uint4*>(p + 3 * HD) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void store(unsigned char* kb, int tid, int vkg, int vch, bool v_thread) const {
+    unsigned char* vb = kb + C::K_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::K_LOADS; ++i) {
+      const int e = tid + NT * i;
+      const int r = e / C::KCH, c = e % C::KCH;
+      *reinterpret_cast<uint4*>(kb + k_off<HD>(r, c)) = k[i];
+    }
+    if (v_thread) {
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int d = vch * 8 + 2 * wd;
+        const uint32_t w0 = comp(v0, wd), w1 = comp(v1, wd), w2 = comp(v2, wd), w3 = comp(v3, wd);
+        uint2 lo, hi;
+        lo.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+        *reinterpret_cast<uint2*>(vb + v_off(d, vkg >> 1) + (vkg & 1) * 8) = lo;
+        *reinterpret_cast<uint2*>(vb + v_off(d + 1, vkg >> 1) + (vkg & 1) * 8) = hi;
+      }
+    }
+  }
+};
+
+template <int HD>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
+  using C = Cfg<HD>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+
+  // ---- workgroup -> (unit = (b, kv head, head chunk), query block), heavy blocks first
+  const int w = blockIdx.x;
+  int unit, qrank;
+  if (gm.xcd_aware) {
+    const int upx = gm.units >> 3;
+    const int j = w >> 3;
+    unit = (w & 7) * upx + j % upx;
+    qrank = j / upx;
+  } else {
+    unit = w % gm.units;
+    qrank = w / gm.units;
+  }
+  const int qb = gm.nqb - 1 - qrank;
+  const int hc = unit % gm.hchunks;
+  const int pair = unit / gm.hchunks;
+  const int kvh = pair % a.KV;
+  const int b = pair / a.KV;
+
+  const int head = kvh * a.group + hc * gm.hpw + (wave % gm.hpw);
+  const int q0 = qb * gm.bm;
+  const int qw0 = q0 + 32 * (wave / gm.hpw);
+  const int qi = qw0 + n;
+  const bool wave_active = qw0 < a.T;
+
+  // ---- Q rows -> B operand (rotated in fp32, rounded to bf16)
+  bf16x8 qf[HD / 16];
+  {
+    const int qrow = min(qi, a.T - 1);
+    const uint4* src =
+        reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + (((long)b * a.H + head) * a.T + qrow) * HD);
+#pragma unroll
+    for (int s = 0; s < HD / 16; ++s) {
+      const uint4 wv = src[2 * s + hf];
+      if (a.rope) {
+        uint32_t d[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float c, sn;
+          rope_cos_sin(a.pos0 + qi, a.freqs.rev[8 * s + 4 * hf + p], c, sn);
+          const uint32_t x = comp(wv, p);
+          const float x0 = bf16_bits_to_f32(x & 0xffffu), x1 = bf16_bits_to_f32(x >> 16);
+          d[p] = pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+        }
+        qf[s] = as_bf16x8(make_uint4(d[0], d[1], d[2], d[3]));
+      } else {
+        qf[s] = as_bf16x8(wv);
+      }
+    }
+  }
+
+  const long kvoff = ((long)b * a.KV + kvh) * (long)a.T * HD;
+  const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k) + kvoff;
+  const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v) + kvoff;
+  const int q_last = min(a.T, q0 + gm.bm) - 1;
+  const int nkt = a.causal ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
+
+  // ---- global -> registers -> LDS staging
+  const int vkg = tid & 15;  // key group (4 keys) of this thread's V unit
+  const int vch = tid >> 4;  // 8-dim chunk of this thread's V unit
+  const bool v_thread = tid < C::V_UNITS;
+  Stage<HD> st;
+  st.load(Kg, Vg, 0, a.T, tid, vkg, vch, v_thread);
+  st.store(smem, tid, vkg, vch, v_thread);
+  __syncthreads();
+
+  f32x16 oacc[HD / 32];
+#pragma unroll
+  for (int mb = 0; mb < HD / 32; ++mb) oacc[mb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+  const float slope2 = a.alibi ? alibi_slope(a.alibi, head, a.H) * 1.4426950408889634f : 0.f;
+  const int krow0 = perm_row(n);
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < nkt) st.load(Kg, Vg, kt + 1, a.T, tid, vkg, vch, v_thread);
+    const int k0 = kt * BN;
+    const bool skip = !wave_active || (a.causal && k0 > qw0 + 31);
+    if (!skip) {
+      const unsigned char* kb = smem + stage * C::STAGE;
+      const unsigned char* vb = kb + C::K_BYTES;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        sacc[kb2] = f32x16{};
+        const int r = 32 * kb2 + krow0;
+#pragma unroll
+        for (int s = 0; s < HD / 16; ++s) {
+          const uint4 av = *reinterpret_cast<const uint4*>(kb + k_off<HD>(r, 2 * s + hf));
+          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), qf[s], sacc[kb2], 0, 0, 0);
+        }
+      }
+      // scores in log2 units; register i of t[] holds key k0 + 32*(i/16) + 16*((i%16)/8) + 8*hf + i%8
+      float t[32];
+      const bool edge = (a.causal && k0 + BN - 1 > qw0) || (k0 + BN > a.T);
+      const int dbase = k0 + 8 * hf - qi;  // key - query for register offset 0
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int koff = 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
+        float x = sacc[i / 16][i % 16];
+        if (a.alibi) {
+          const float dk = (float)(dbase + koff);
+          x = fmaf(x, c2, slope2 * (a.causal ? dk : -fabsf(dk)));
+        } else {
+          x *= c2;
+        }
+        if (edge) {
+          const int key = k0 + 8 * hf + koff;
+          const bool vis = key < a.T && (!a.causal || key <= qi);
+          x = vis ? x : -INFINITY;
+        }
+        t[i] = x;
+      }
+      float mx = t[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, t[i]);
+      mx = fmaxf(mx, xhalf(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        t[i] = __builtin_amdgcn_exp2f(t[i] - m_new);
+        lsum += t[i];
+      }
+      l_run = fmaf(l_run, alpha, lsum);
+      m_run = m_new;
+#pragma unroll
+      for (int mb = 0; mb < HD / 32; ++mb) oacc[mb] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint4 pw;
+        pw.x = pack_bf16x2(t[8 * u + 0], t[8 * u + 1]);
+        pw.y = pack_bf16x2(t[8 * u + 2], t[8 * u + 3]);
+        pw.z = pack_bf16x2(t[8 * u + 4], t[8 * u + 5]);
+        pw.w = pack_bf16x2(t[8 * u + 6], t[8 * u + 7]);
+        const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+        for (int mb = 0; mb < HD / 32; ++mb) {
+          const uint4 av = *reinterpret_cast<const uint4*>(vb + v_off(32 * mb + n, 2 * u + hf));
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pb, oacc[mb], 0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < nkt) st.store(smem + (stage ^ 1) * C::STAGE, tid, vkg, vch, v_thread);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_run + xhalf(l_run);
+  if (qi >= a.T) return;
+  const float inv_l = 1.0f / l_tot;
+  const long orow = (((long)b * a.H + head) * a.T + qi) * HD;
+#pragma unroll
+  for (int mb = 0; mb < HD / 32; ++mb) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * mb + 8 * g4 + 4 * hf;
+      const float o0 = oacc[mb][4 * g4 + 0] * inv_l, o1 = oacc[mb][4 * g4 + 1] * inv_l;
+      const float o2 = oacc[mb][4 * g4 + 2] * inv_l, o3 = oacc[mb][4 * g4 + 3] * inv_l;
+      if (a.out_bf16) {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + d) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  }
+  if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.T + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+}
+
+GridMap make_grid(const PrefillArgs& a) {
+  GridMap gm;
+  gm.hpw = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
+  gm.hchunks = a.group / gm.hpw;
+  gm.bm = 32 * (NW / gm.hpw);
+  gm.nqb = (a.T + gm.bm - 1) / gm.bm;
+  gm.units = a.B * a.KV * gm.hchunks;
+  gm.xcd_aware = (gm.units % 8) == 0;
+  return gm;
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(const PrefillArgs& a, int bf16) {
+  if (!bf16 || (a.hd != 64 && a.hd != 128)) return false;
+  const GridMap gm = make_grid(a);
+  return (long)gm.units * gm.nqb < (1L << 31);
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
+  const GridMap gm = make_grid(a);
+  const dim3 grid((unsigned)(gm.units * gm.nqb));
+  if (a.hd == 128) {
+    hipLaunchKernelGGL(prefill_mfma_kernel<128>, grid, dim3(NT), 0, s, a, gm);
+  } else {
+    hipLaunchKernelGGL(prefill_mfma_kernel<64>, grid, dim3(NT), 0, s, a, gm);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace attn
