@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  1. prefill: causal GQA + RoPE attention forward, Llama-3-8B shape
+     (B=4, T=4096, H=32, KV=8, hd=128, RoPE base 5e5, bf16 in, bf16 out);
+  2. decode: one KV-cache decode step for 64 sequences with context lengths
+     drawn uniformly from [512, 8192] (H=32, KV=8, hd=128, RoPE base 1e4).
+
+Prints ONE JSON line. ``value`` is prefill TFLOP/s (algorithmic flops
+4*B*H*hd*T(T+1)/2 over the time of the prefill call); the decode KV-read GB/s
+(sum over sequences of (len+1)*KV*hd*2*2 bytes over the time of the decode
+call) is in ``decode``. ``roofline`` is for the dominant kernel (the prefill
+attention kernel), timed with HIP events that the library records around that
+kernel on its own stream; ``decode.roofline`` is the same for the split-KV
+kernel. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
+same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|prefill|decode|alibi|small]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA+RoPE attn fwd TFLOP/s (prefill) + KV-read GB/s (decode), 1 GPU"
+# MI355X: 256 CUs x 4096 dense bf16 flop/clk/CU x 2.4 GHz; HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (same SONAME)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreate.restype = ctypes.c_int
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.restype = ctypes.c_int
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.made.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel)
+    if not ent or ent.get("source_digest") != source_digest(sources):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+PREFILL_SOURCES = ["transformer_attention_02_amd/csrc/prefill_mfma.hip", "transformer_attention_02_amd/csrc/attn_internal.h"]
+DECODE_SOURCES = ["transformer_attention_02_amd/csrc/decode.hip", "transformer_attention_02_amd/csrc/attn_internal.h"]
+
+
+class Prefill:
+    def __init__(self, w, dev, bd, W, torch):
+        self.w, self.bd = w, bd
+        q, k, v = W.prefill_inputs(w)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.out = torch.empty(w.B, w.H, w.T, w.hd, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(w.B, w.H, w.T, dtype=torch.float32, device=dev)
+        dt = bd.ATTN_DTYPE_BF16 if w.dtype == "bf16" else bd.ATTN_DTYPE_F32
+        self.dt = dt
+        self.ws, self.ws_bytes = bd.prefill_workspace(w.B, w.T, w.KV, w.hd, dt, w.rope_base, dev)
+
+    def __call__(self, stream, events=None):
+        w, bd = self.w, self.bd
+        if events:
+            bd.attn_set_timing_events(*events)
+        st = bd.attn_prefill_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
+                                 self.lse.data_ptr(), w.B, w.T, w.H, w.KV, w.hd, w.pos0, w.rope_base,
+                                 int(w.causal), w.alibi, self.dt, bd.ATTN_DTYPE_BF16, self.ws.data_ptr(),
+                                 self.ws_bytes, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_prefill_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+    def work(self):
+        return self.w.flops()
+
+
+class Decode:
+    def __init__(self, w, dev, bd, W, torch):
+        self.w, self.bd = w, bd
+        inp = W.decode_inputs(w, device=dev)
+        self.inp = inp
+        self.q, self.kn, self.vn = inp.q.to(dev), inp.k_new.to(dev), inp.v_new.to(dev)
+        self.kc, self.vc = inp.k_cache, inp.v_cache
+        self.lens = torch.from_numpy(inp.lens).to(dev)
+        self.Lmax = self.kc.shape[2]
+        self.out = torch.empty(inp.q.shape, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
+        self.ws, self.ws_bytes = bd.decode_workspace(w.B, w.H, w.KV, w.hd, self.Lmax, dev)
+
+    def __call__(self, stream, events=None):
+        w, bd = self.w, self.bd
+        if events:
+            bd.attn_set_timing_events(*events)
+        st = bd.attn_decode_fwd(self.q.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), self.kc.data_ptr(),
+                                self.vc.data_ptr(), self.lens.data_ptr(), self.out.data_ptr(), self.lse.data_ptr(),
+                                w.B, w.H, w.KV, w.hd, self.Lmax, w.rope_base, w.alibi, bd.ATTN_DTYPE_BF16,
+                                bd.ATTN_DTYPE_BF16, self.ws.data_ptr(), self.ws_bytes, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_decode_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+    def work(self):
+        return self.w.kv_read_bytes()
+
+
+def cpu_baseline_leg(pre, dec, heads, seqs):
+    """The fp64 oracle on a bounded sample of the same workload (rank 0, N=1 only)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_decode, attention_prefill
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    res = {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count()}
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    if pre is not None:
+        w = pre.w
+        g = w.H // w.KV
+        heads = max(g, heads // g * g)
+        qs, ks, vs = f64(pre.q[0:1, :heads]), f64(pre.k[0:1, :heads // g]), f64(pre.v[0:1, :heads // g])
+        t0 = time.perf_counter()
+        ref, _ = attention_prefill(qs, ks, vs, pos0=w.pos0, rope_base=w.rope_base, causal=w.causal, alibi=w.alibi)
+        dt = time.perf_counter() - t0
+        flops = 4.0 * heads * w.hd * (w.T * (w.T + 1) / 2 if w.causal else w.T * w.T)
+        err = float(np.abs(f64(pre.out[0:1, :heads]) - ref).max())
+        res.update(value=flops / dt / 1e12, unit="TFLOP/s", seconds=dt,
+                   sample=f"{heads} query heads of batch 0 ({heads // g} KV heads), all {w.T} causal rows: "
+                          f"{flops / w.flops() * 100:.2f}% of the prefill step",
+                   max_abs_err_vs_gpu_bf16_out=err)
+    if dec is not None:
+        w = dec.w
+        lens = dec.inp.lens
+        pick = list(range(min(seqs, w.B)))
+        t_total = 0.0
+        nbytes = 0
+        errs = []
+        for b in pick:
+            L = int(lens[b])
+            kc = f64(dec.kc[b:b + 1, :, :L])
+            vc = f64(dec.vc[b:b + 1, :, :L])
+            t0 = time.perf_counter()
+            ref, _, _, _ = attention_decode(f64(dec.q[b:b + 1]), f64(dec.kn[b:b + 1]), f64(dec.vn[b:b + 1]), kc, vc,
+                                            np.array([L], dtype=np.int32), rope_base=w.rope_base, alibi=w.alibi)
+            t_total += time.perf_counter() - t0
+            nbytes += (L + 1) * w.KV * w.hd * 2 * 2
+            errs.append(float(np.abs(f64(dec.out[b:b + 1]) - ref).max()))
+        res["decode"] = {"value": nbytes / t_total / 1e9, "unit": "GB/s", "seconds": t_total,
+                         "sample": f"sequences 0..{len(pick) - 1} of {w.B}", "max_abs_err_vs_gpu_bf16_out": max(errs)}
+        if pre is None:
+            res.update(value=res["decode"]["value"], unit="GB/s", seconds=t_total, sample=res["decode"]["sample"])
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all", choices=["all", "prefill", "decode", "alibi", "small"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "multi-GPU sharding is described in DESIGN.md and not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from transformer_attention_02_amd import binding as bd
+    from transformer_attention_02_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    bd.load()
+    dev = torch.device("cuda:0")
+    hip = HipEvents()
+
+    pre_w = {"all": W.LLAMA3_8B, "prefill": W.LLAMA3_8B, "alibi": W.ALIBI_MHA, "small": W.SMALL_BF16}.get(args.workload)
+    pre = Prefill(pre_w, dev, bd, W, torch) if pre_w is not None else None
+    dec = Decode(W.KV_DECODE, dev, bd, W, torch) if args.workload in ("all", "decode") else None
+    log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None}")
+
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        if pre:
+            pre(stream)
+        if dec:
+            dec(stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk")}
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        if pre:
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["pc"][i][0]), ctypes.c_void_p(stream))
+            pre(stream, ev["pk"][i])
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["pc"][i][1]), ctypes.c_void_p(stream))
+        if dec:
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][0]), ctypes.c_void_p(stream))
+            dec(stream, ev["dk"][i])
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][1]), ctypes.c_void_p(stream))
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+
+    def avg(key):
+        return sum(hip.elapsed_ms(a, b) for a, b in ev[key]) / K
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": total_ms / K,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16; random lengths for decode)"}
+    cfg = {}
+    if pre:
+        w = pre.w
+        pc, pk = avg("pc"), avg("pk")
+        tflops = w.flops() / (pc * 1e-3) / 1e12
+        kt = w.flops() / (pk * 1e-3) / 1e12
+        line.update(value=tflops, unit="TFLOP/s")
+        cfg["workload"] = w.name
+        cfg["prefill"] = {"B": w.B, "T": w.T, "H": w.H, "KV": w.KV, "hd": w.hd, "rope_base": w.rope_base,
+                          "causal": w.causal, "alibi": w.alibi, "out_dtype": "bf16", "flops": w.flops(),
+                          "call_ms": pc, "kernel_ms": pk}
+        traffic = traffic_for("prefill_mfma_kernel", PREFILL_SOURCES)
+        line["roofline"] = {"bound": "mfma", "achieved": kt, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": kt / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": "prefill_mfma_kernel<128>"}
+    if dec:
+        w = dec.w
+        dc, dk = avg("dc"), avg("dk")
+        gbs = w.kv_read_bytes() / (dc * 1e-3) / 1e9
+        kg = w.kv_read_bytes() / (dk * 1e-3) / 1e9
+        dline = {"value": gbs, "unit": "GB/s", "call_ms": dc, "kernel_ms": dk, "kv_bytes": w.kv_read_bytes(),
+                 "roofline": {"bound": "hbm", "achieved": kg, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": kg / PEAK_HBM_GBS, "traffic": traffic_for("decode_split", DECODE_SOURCES),
+                              "kernel": "decode split-KV kernel"}}
+        cfg["decode"] = {"B": w.B, "H": w.H, "KV": w.KV, "hd": w.hd, "len_range": [w.len_lo, w.len_hi],
+                         "len_seed": w.len_seed, "Lmax": dec.Lmax, "rope_base": w.rope_base, "out_dtype": "bf16"}
+        line["decode"] = dline
+        if not pre:
+            line.update(value=gbs, unit="GB/s", roofline=dline["roofline"])
+            cfg["workload"] = w.name
+        else:
+            cfg["workload"] = cfg["workload"] + " + " + w.name
+    line["config"] = cfg
+    torch.cuda.synchronize()
+    ok = True
+    if pre:
+        ok &= bool(torch.isfinite(pre.out).all().item())
+    if dec:
+        ok &= bool(torch.isfinite(dec.out).all().item())
+    line["outputs_finite"] = ok
+    hip.close()
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_leg(pre, dec, args.cpu_heads, args.cpu_seqs)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,6 +73,16 @@ const char* attn_status_str(int status);
 const char* attn_last_error(void);
 
 /*
+ * Timing hook for benchmarks and profilers. `start` and `stop` are hipEvent_t
+ * handles created by the caller (or NULL to clear). The next attn_prefill_fwd
+ * or attn_decode_fwd call made by the same thread records `start` on its
+ * stream immediately before launching its main kernel (the attention kernel of
+ * prefill, the split-KV kernel of decode) and `stop` immediately after it, then
+ * clears the hook. The events stay owned by the caller. Always returns ATTN_OK.
+ */
+int attn_set_timing_events(void* start, void* stop);
+
+/*
  * Bytes of device workspace attn_prefill_fwd needs: the rotated keys,
  * B*KV*T*hd elements of `dtype`, when rope_base != 0; 0 without rotary
  * embedding. Returns 0 for invalid sizes (the forward call reports why).
@@ -99,8 +109,9 @@ size_t attn_prefill_workspace_bytes(int B, int T, int KV, int hd, int dtype, dou
  *   workspace: device scratch of at least attn_prefill_workspace_bytes(...)
  *   bytes (may be NULL when that figure is 0); its contents are clobbered.
  *
- * q, k, v, out and workspace must not overlap. Runs the MFMA kernel for bf16
- * with hd in {64,128} and H/KV dividing 8, and a vector-ALU kernel otherwise.
+ * q, k, v, out and workspace must not overlap. bf16 inputs with hd in
+ * {64,128} run on the matrix-core (MFMA) kernel; every other supported case
+ * runs on a vector-ALU kernel with fp32 arithmetic throughout.
  */
 int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      int B, int T, int H, int KV, int hd, int pos0, double rope_base,
@@ -128,9 +139,11 @@ size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax);
  *   v_cache    [B, KV, Lmax, hd]  dtype, values at slots 0..L-1 (read);
  *                                 slot L receives v_new (written)
  *   cache_lens [B] int32 device   L = cache_lens[b] >= 0 tokens already cached;
- *                                 must satisfy L < Lmax (not checked on the host,
- *                                 which does not read device memory; a device
- *                                 side clamp keeps accesses in bounds)
+ *                                 must satisfy L < Lmax. The host does not read
+ *                                 device memory, so this is checked on the
+ *                                 device: a sequence with L outside [0, Lmax)
+ *                                 gets NaN in out and lse and its cache rows
+ *                                 are neither read nor written.
  *   out        [B, H, hd]         out_dtype (written)
  *   lse        [B, H]             fp32 (written); may be NULL
  *   The new token sits at position L: its query and key are rotated at L and

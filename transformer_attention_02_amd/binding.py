@@ -36,6 +36,7 @@ EXPORTS = (
     "attn_abi_version",
     "attn_status_str",
     "attn_last_error",
+    "attn_set_timing_events",
     "attn_prefill_workspace_bytes",
     "attn_prefill_fwd",
     "attn_decode_workspace_bytes",
@@ -51,6 +52,7 @@ _SIGS = {
     "attn_abi_version": (_I, []),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
+    "attn_set_timing_events": (_I, [_P, _P]),
     "attn_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _D]),
     "attn_prefill_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I, _I, _I, _P, _S, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
@@ -97,6 +99,10 @@ status_str = attn_status_str
 
 def attn_last_error() -> str:
     return load().attn_last_error().decode()
+
+
+def attn_set_timing_events(start, stop) -> int:
+    return load().attn_set_timing_events(start, stop)
 
 
 def attn_prefill_workspace_bytes(B, T, KV, hd, dtype, rope_base) -> int:

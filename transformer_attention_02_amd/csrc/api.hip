@@ -16,6 +16,14 @@ using namespace attn;
 namespace {
 
 thread_local std::string g_last_error;
+thread_local TimingHook g_timing;
+
+// Takes (and clears) this thread's timing hook.
+TimingHook take_timing() {
+  TimingHook t = g_timing;
+  g_timing = TimingHook();
+  return t;
+}
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
@@ -89,6 +97,12 @@ const char* attn_status_str(int status) {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
+int attn_set_timing_events(void* start, void* stop) {
+  g_timing.start = reinterpret_cast<hipEvent_t>(start);
+  g_timing.stop = reinterpret_cast<hipEvent_t>(stop);
+  return ATTN_OK;
+}
+
 size_t attn_prefill_workspace_bytes(int B, int T, int KV, int hd, int dtype, double rope_base) {
   if (B <= 0 || T <= 0 || KV <= 0 || hd <= 0 || rope_base == 0.0) return 0;
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return 0;
@@ -155,8 +169,14 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
     if (int c = hip_status(launch_rope_k(r, bf16, s), "rope_k launch")) return c;
     a.k = workspace;
   }
-  if (prefill_mfma_supported(a, bf16)) return hip_status(launch_prefill_mfma(a, s), "prefill_mfma launch");
-  return hip_status(launch_prefill_valu(a, bf16, s), "prefill_valu launch");
+  const TimingHook tm = take_timing();
+  if (int c = hip_status(tm.before(s), "timing event")) return c;
+  if (prefill_mfma_supported(a, bf16)) {
+    if (int c = hip_status(launch_prefill_mfma(a, s), "prefill_mfma launch")) return c;
+  } else {
+    if (int c = hip_status(launch_prefill_valu(a, bf16, s), "prefill_valu launch")) return c;
+  }
+  return hip_status(tm.after(s), "timing event");
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax) {
@@ -214,7 +234,8 @@ int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k
   a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
   a.freqs = make_freqs(hd, rope_base);
-  return hip_status(launch_decode(a, dtype == ATTN_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream)),
+  const TimingHook tm = take_timing();
+  return hip_status(launch_decode(a, dtype == ATTN_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream), tm),
                     "decode launch");
 }
 

@@ -61,11 +61,19 @@ struct DecodeArgs {
   RopeFreqs freqs;
 };
 
+// Events recorded around the main kernel of one call (either may be null).
+struct TimingHook {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  hipError_t before(hipStream_t s) const { return start ? hipEventRecord(start, s) : hipSuccess; }
+  hipError_t after(hipStream_t s) const { return stop ? hipEventRecord(stop, s) : hipSuccess; }
+};
+
 hipError_t launch_rope_k(const RopeKArgs& a, int bf16, hipStream_t s);
 hipError_t launch_prefill_valu(const PrefillArgs& a, int bf16, hipStream_t s);
 bool prefill_mfma_supported(const PrefillArgs& a, int bf16);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s, const TimingHook& tm);
 
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIPCC__)

@@ -162,33 +162,35 @@ __global__ void decode_merge_kernel(DecodeArgs a) {
 }
 
 template <int BF16, int HD>
-hipError_t launch_decode_hd(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_hd(const DecodeArgs& a, hipStream_t s, const TimingHook& tm) {
   hipLaunchKernelGGL(decode_append_kernel<BF16>, dim3(a.KV, a.B), dim3(HD / 2), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if ((e = tm.before(s)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_valu_kernel<BF16, HD>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if ((e = tm.after(s)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<HD>), dim3(a.H, a.B), dim3(HD), 0, s, a);
   return hipGetLastError();
 }
 
 template <int BF16>
-hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t s, const TimingHook& tm) {
   switch (a.hd) {
-    case 8: return launch_decode_hd<BF16, 8>(a, s);
-    case 16: return launch_decode_hd<BF16, 16>(a, s);
-    case 32: return launch_decode_hd<BF16, 32>(a, s);
-    case 64: return launch_decode_hd<BF16, 64>(a, s);
-    case 128: return launch_decode_hd<BF16, 128>(a, s);
+    case 8: return launch_decode_hd<BF16, 8>(a, s, tm);
+    case 16: return launch_decode_hd<BF16, 16>(a, s, tm);
+    case 32: return launch_decode_hd<BF16, 32>(a, s, tm);
+    case 64: return launch_decode_hd<BF16, 64>(a, s, tm);
+    case 128: return launch_decode_hd<BF16, 128>(a, s, tm);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s) {
-  return bf16 ? launch_decode_dt<1>(a, s) : launch_decode_dt<0>(a, s);
+hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s, const TimingHook& tm) {
+  return bf16 ? launch_decode_dt<1>(a, s, tm) : launch_decode_dt<0>(a, s, tm);
 }
 
 }  // namespace attn
