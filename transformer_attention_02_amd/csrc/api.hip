@@ -119,7 +119,8 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
     return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d KV=%d)", B, T, H, KV);
   if (H % KV) return fail(ATTN_ERR_SHAPE, "H=%d is not a multiple of KV=%d", H, KV);
   if (pos0 < 0 || (long long)pos0 + T > 0x7fffffffLL) return fail(ATTN_ERR_SHAPE, "pos0=%d out of range", pos0);
-  if (H > 65535 || B > 65535) return fail(ATTN_ERR_SHAPE, "H and B must be <= 65535");
+  if (H > 65535 || B > 65535 || (long long)B * KV > 65535 * 8LL)
+    return fail(ATTN_ERR_SHAPE, "H, B and B*KV/8 must be <= 65535");
   if (int c = check_common(dtype, out_dtype, alibi, rope_base, hd)) return c;
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_UNSUPPORTED, "causal %d", causal);
   if ((long long)B * H * T * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "tensor too large");
@@ -161,7 +162,7 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
     RopeKArgs r;
     r.k = k;
     r.kr = workspace;
-    r.rows = (long)B * KV * T;
+    r.heads = B * KV;
     r.T = T;
     r.hd = hd;
     r.pos0 = pos0;
@@ -179,12 +180,26 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
   return hip_status(tm.after(s), "timing event");
 }
 
+namespace {
+// Workspace layout (sized for the smaller split, so it fits either kernel):
+// [part_o: rows*hd fp32][part_ml: rows float2][q_rot: B*H*hd bf16], rows = B*H*ceil(Lmax/256).
+struct DecodeWs {
+  long long part_o, part_ml, q_rot, total;
+};
+DecodeWs decode_ws_layout(int B, int H, int hd, int Lmax) {
+  const long long rows = (long long)B * H * ((Lmax + kDecodeSplit - 1) / kDecodeSplit);
+  DecodeWs w;
+  w.part_o = 0;
+  w.part_ml = rows * hd * 4;
+  w.q_rot = (w.part_ml + rows * 8 + 255) / 256 * 256;
+  w.total = (w.q_rot + (long long)B * H * hd * 2 + 255) / 256 * 256;
+  return w;
+}
+}  // namespace
+
 size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax) {
   if (B <= 0 || H <= 0 || KV <= 0 || hd <= 0 || Lmax <= 0) return 0;
-  const long long nsplit = (Lmax + kDecodeSplit - 1) / kDecodeSplit;
-  const long long rows = (long long)B * H * nsplit;
-  const long long bytes = rows * hd * 4 + rows * 8;
-  return (size_t)((bytes + 255) / 256 * 256);
+  return (size_t)decode_ws_layout(B, H, hd, Lmax).total;
 }
 
 int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -225,10 +240,13 @@ int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k
   a.hd = hd;
   a.group = H / KV;
   a.Lmax = Lmax;
+  const DecodeWs lay = decode_ws_layout(B, H, hd, Lmax);
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+  a.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
+  a.q_rot = reinterpret_cast<uint16_t*>(ws + lay.q_rot);
+  a.split = kDecodeSplit;  // the launcher sets the split of the kernel it picks
   a.nsplit = (Lmax + kDecodeSplit - 1) / kDecodeSplit;
-  const long long rows = (long long)B * H * a.nsplit;
-  a.part_o = reinterpret_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(workspace) + rows * hd * 4);
   a.rope = rope_base != 0.0;
   a.alibi = alibi;
   a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;

@@ -9,7 +9,8 @@
 namespace attn {
 
 constexpr int kMaxHeadDim = 128;
-constexpr int kDecodeSplit = 256;  // keys per split-KV partial in decode
+constexpr int kDecodeSplit = 256;  // keys per split-KV partial, vector-ALU decode kernel
+constexpr int kSplitMfma = 512;    // keys per split-KV partial, MFMA decode kernel
 
 // 4 theta_i / (2 pi) in fp64 (quarter turns per position) for i = 0 .. hd/2-1,
 // theta_i = base^(-2i/hd).
@@ -35,9 +36,9 @@ struct PrefillArgs {
 };
 
 struct RopeKArgs {
-  const void* k;  // [rows, hd] raw
-  void* kr;       // [rows, hd] rotated
-  long rows;      // B*KV*T
+  const void* k;  // [heads, T, hd] raw
+  void* kr;       // [heads, T, hd] rotated
+  int heads;      // B*KV
   int T, hd, pos0;
   RopeFreqs freqs;
 };
@@ -53,7 +54,10 @@ struct DecodeArgs {
   float* lse;            // [B,H] or nullptr
   float* part_o;         // [B,H,nsplit,hd]
   float2* part_ml;       // [B,H,nsplit]  (running max in log2 units, denominator)
-  int B, H, KV, hd, group, Lmax, nsplit;
+  uint16_t* q_rot;       // [B,H,hd] bf16 query rotated at L (MFMA path)
+  int B, H, KV, hd, group, Lmax;
+  int split;             // key slots per partial
+  int nsplit;            // partial slots per (b, h): ceil(Lmax / split)
   int rope;
   int alibi;
   int out_bf16;

@@ -29,27 +29,32 @@ __device__ __forceinline__ float ld(const void* base, long i) {
 
 __device__ __forceinline__ bool bad_len(int L, int Lmax) { return L < 0 || L >= Lmax; }
 
-// Grid (KV, B), hd/2 threads: rotate k_new at L and write slot L of both caches.
+// Grid (KV, B), hd/2 threads (one interleaved pair each): rotate k_new at L and
+// write slot L of both caches; for the MFMA path also rotate the group's query
+// heads at L (same cos/sin) into q_rot as bf16.
 template <int BF16>
 __global__ void decode_append_kernel(DecodeArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, p = threadIdx.x;
   const int L = a.lens[b];
   if (bad_len(L, a.Lmax) || 2 * p >= a.hd) return;
+  float c = 1.f, s = 0.f;
+  if (a.rope) rope_cos_sin(L, a.freqs.rev[p], c, s);
   const long src = ((long)b * a.KV + g) * a.hd + 2 * p;
   const long dst = (((long)b * a.KV + g) * a.Lmax + L) * a.hd + 2 * p;
-  float x0 = ld<BF16>(a.k_new, src), x1 = ld<BF16>(a.k_new, src + 1);
-  if (a.rope) {
-    float c, s;
-    rope_cos_sin(L, a.freqs.rev[p], c, s);
-    const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
-    x0 = y0;
-    x1 = y1;
-  }
+  const float x0 = ld<BF16>(a.k_new, src), x1 = ld<BF16>(a.k_new, src + 1);
+  const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
   if constexpr (BF16) {
-    reinterpret_cast<uint32_t*>(a.k_cache)[dst >> 1] = pack_bf16x2(x0, x1);
+    reinterpret_cast<uint32_t*>(a.k_cache)[dst >> 1] = pack_bf16x2(y0, y1);
     reinterpret_cast<uint32_t*>(a.v_cache)[dst >> 1] = reinterpret_cast<const uint32_t*>(a.v_new)[src >> 1];
+    if (a.q_rot) {
+      for (int j = 0; j < a.group; ++j) {
+        const long qi = ((long)b * a.H + g * a.group + j) * a.hd + 2 * p;
+        const float q0 = ld<BF16>(a.q, qi), q1 = ld<BF16>(a.q, qi + 1);
+        reinterpret_cast<uint32_t*>(a.q_rot)[qi >> 1] = pack_bf16x2(q0 * c - q1 * s, q0 * s + q1 * c);
+      }
+    }
   } else {
-    reinterpret_cast<float2*>(a.k_cache)[dst >> 1] = make_float2(x0, x1);
+    reinterpret_cast<float2*>(a.k_cache)[dst >> 1] = make_float2(y0, y1);
     reinterpret_cast<float2*>(a.v_cache)[dst >> 1] = reinterpret_cast<const float2*>(a.v_new)[src >> 1];
   }
 }
@@ -128,50 +133,303 @@ __global__ __launch_bounds__(256) void decode_split_valu_kernel(DecodeArgs a) {
   if (t == 0) a.part_ml[pidx] = make_float2(mx, sm);
 }
 
-// Merge the partials of one (b, h). Grid (H, B), hd threads.
+// ---------------------------------------------------------------- MFMA split kernel
+// bf16, hd in {64, 128}, group = H/KV <= 16. Grid (nsplit, KV, B), 4 waves,
+// kSplitMfma key slots per workgroup.
+// The group's query heads are the columns of S^T = K Q^T computed with
+// v_mfma_f32_16x16x32_bf16, so each K/V byte is read from memory once for all of
+// them. Each wave streams 32-key tiles (interleaved with the other waves) through
+// a private LDS region, with the next tile's global loads in flight while the
+// current one is computed (no workgroup barrier inside the loop). K is stored
+// row-major with an XOR swizzle and read as the A operand; V is stored row-major
+// with an XOR swizzle and read as V^T with ds_read_b64_tr_b16, the transposing
+// LDS load of gfx950. Key rows are permuted so that a lane's accumulator
+// registers hold 8 consecutive keys, which feed O^T = V^T P^T as its B operand
+// straight from registers. The query arrives rotated (the append kernel rotates
+// it once per head). The four waves' (m, l, O) are merged in LDS and one partial
+// per head is written.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 32;  // keys per wave tile
+constexpr int kWaves = 4;
+constexpr int kTilesPerWave = kSplitMfma / (kWaves * kTile);
+
+// MFMA row rho (0..15) of key block kb (0 or 1) holds tile key 8*(rho/4) + 4*kb + rho%4.
+__device__ __forceinline__ int kperm16(int rho, int kb) { return ((rho >> 2) << 3) | (kb << 2) | (rho & 3); }
+
 template <int HD>
-__global__ void decode_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__device__ __forceinline__ int dk_off(int r, int c) {  // K tile: 16-byte chunk c of key row r
+  if constexpr (HD == 128) {
+    return r * 256 + ((c ^ ((r & 3) | ((r >> 3) << 2))) << 4);
+  } else {
+    return r * 128 + ((c ^ (((r >> 1) & 1) | ((r >> 3) << 1))) << 4);
+  }
+}
+template <int HD>
+__device__ __forceinline__ int dv_off(int r, int c) {  // V tile: 16-byte chunk c of key row r
+  if constexpr (HD == 128) {
+    return r * 256 + ((c ^ (((r & 3) << 1) | (((r >> 3) & 1) << 3))) << 4);
+  } else {
+    return r * 128 + ((c ^ ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2))) << 4);
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_split_mfma_kernel(DecodeArgs a) {
+  constexpr int KCH = HD / 8;                 // 16-byte chunks per row
+  constexpr int TILE_BYTES = kTile * HD * 2;  // one K or V tile
+  constexpr int LOADS = kTile * KCH / 64;     // 16-byte loads per lane per tensor
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * 2 * TILE_BYTES];
+  __shared__ float mer_m[kWaves][16];
+  __shared__ float mer_l[kWaves][16];
+
+  const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int L = a.lens[b];
+  if (bad_len(L, a.Lmax)) return;
+  const int nk = L + 1;
+  const int k0 = sp * kSplitMfma;
+  if (k0 >= nk) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int G = a.group;
+  const bool qcol = n < G;
+  const int head = kvh * G + (qcol ? n : 0);
+
+  // Q^T B operand (rotated at L by the append kernel): column n, k-step s -> dims 32s + 8g .. +7
+  bf16x8_t qf[HD / 32];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.q_rot + ((long)b * a.H + head) * HD);
+#pragma unroll
+    for (int s = 0; s < HD / 32; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8_t, qcol ? src[4 * s + g] : make_uint4(0, 0, 0, 0));
+  }
+  const float c2 = a.scale_log2;
+  const float slope2 = a.alibi ? alibi_slope(a.alibi, head, a.H) * kLog2e : 0.f;
+
+  const long cbase = ((long)b * a.KV + kvh) * (long)a.Lmax * HD;
+  const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k_cache) + cbase;
+  const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v_cache) + cbase;
+  unsigned char* kl = smem + wave * 2 * TILE_BYTES;
+  unsigned char* vl = kl + TILE_BYTES;
+
+  f32x4_t oacc[HD / 16];
+#pragma unroll
+  for (int db = 0; db < HD / 16; ++db) oacc[db] = f32x4_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  uint4 kr[LOADS], vr[LOADS];
+  auto load_tile = [&](int ts) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = lane + 64 * i;
+      const int r = e / KCH, c = e % KCH;
+      const bool in = ts + r < nk;
+      const long off = (long)(ts + r) * HD + c * 8;
+      kr[i] = in ? *reinterpret_cast<const uint4*>(Kg + off) : make_uint4(0, 0, 0, 0);
+      vr[i] = in ? *reinterpret_cast<const uint4*>(Vg + off) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_tile(k0 + wave * kTile);
+
+#pragma unroll 1
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    const int ts = k0 + (t * kWaves + wave) * kTile;
+    if (ts >= nk) break;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = lane + 64 * i;
+      const int r = e / KCH, c = e % KCH;
+      *reinterpret_cast<uint4*>(kl + dk_off<HD>(r, c)) = kr[i];
+      *reinterpret_cast<uint4*>(vl + dv_off<HD>(r, c)) = vr[i];
+    }
+    const int tn = ts + kWaves * kTile;
+    if (t + 1 < kTilesPerWave && tn < nk) load_tile(tn);
+
+    // S^T = K Q^T for the tile's two 16-key blocks
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4_t{};
+      const int row = kperm16(n, kb);
+#pragma unroll
+      for (int s = 0; s < HD / 32; ++s) {
+        const uint4 av = *reinterpret_cast<const uint4*>(kl + dk_off<HD>(row, 4 * s + g));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), qf[s], sacc[kb], 0, 0, 0);
+      }
+    }
+    // tv[4*kb + r] is key ts + 8g + 4kb + r
+    float tv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = ts + 8 * g + i;
+      float x = sacc[i >> 2][i & 3] * c2;
+      if (a.alibi) x = fmaf(slope2, (float)(key - L), x);
+      x = key < nk ? x : -INFINITY;
+      tv[i] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tv[i] = __builtin_amdgcn_exp2f(tv[i] - m_new);
+      lsum += tv[i];
+    }
+    l_run = fmaf(l_run, alpha, lsum);
+    m_run = m_new;
+    const bf16x8_t pb = __builtin_bit_cast(
+        bf16x8_t, make_uint4(pack_bf16x2(tv[0], tv[1]), pack_bf16x2(tv[2], tv[3]), pack_bf16x2(tv[4], tv[5]),
+                             pack_bf16x2(tv[6], tv[7])));
+    // O^T += V^T P^T. Transposing load: source lane i of 16-lane group g points at
+    // row 8g + i/4 (+4), columns d0 + 4*(i%4); lane i receives V[rows][d0 + i].
+    const int li = lane & 15;
+#pragma unroll
+    for (int db = 0; db < HD / 16; ++db) {
+      oacc[db] *= alpha;
+      const int col = 16 * db + 4 * (li & 3);
+      const int r = 8 * g + (li >> 2);
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(vl + dv_off<HD>(r, col >> 3) + (col & 7) * 2));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(vl + dv_off<HD>(r + 4, col >> 3) + (col & 7) * 2));
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, oacc[db], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the four waves: per column n, M = max_w m_w, weights 2^(m_w - M)
+  float l_col = l_run + __shfl_xor(l_run, 16);
+  l_col += __shfl_xor(l_col, 32);
+  if (g == 0) {
+    mer_m[wave][n] = m_run;
+    mer_l[wave][n] = l_col;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mer_m[w][n]);
+  const float wgt = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  float* ob = reinterpret_cast<float*>(smem);  // [wave][16][HD], reuses the tile space
+  if (qcol) {
+#pragma unroll
+    for (int db = 0; db < HD / 16; ++db) {
+      const int d = 16 * db + 4 * g;
+      *reinterpret_cast<float4*>(ob + (wave * 16 + n) * HD + d) =
+          make_float4(oacc[db][0] * wgt, oacc[db][1] * wgt, oacc[db][2] * wgt, oacc[db][3] * wgt);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * HD; e += 256) {
+    const int col = e / HD, d = e % HD;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) o += ob[(w * 16 + col) * HD + d];
+    const long pidx = ((long)b * a.H + kvh * G + col) * a.nsplit + sp;
+    a.part_o[pidx * HD + d] = o;
+    if (d == 0) {
+      float Mc = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) Mc = fmaxf(Mc, mer_m[w][col]);
+      float lt = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = mer_m[w][col];
+        lt += (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mc) * mer_l[w][col];
+      }
+      a.part_ml[pidx] = make_float2(Mc, lt);
+    }
+  }
+}
+
+// Merge the partials of one (b, h): one wave, lanes in parallel over splits for
+// the max and the weights, then each lane accumulates two head-dim entries over
+// the splits (independent loads). Grid (H, B), 64 threads.
+template <int HD>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int L = a.lens[b];
   const long orow = ((long)b * a.H + h) * HD;
-  float res, lse;
+  float res[2] = {0.f, 0.f};
+  float lse;
   if (bad_len(L, a.Lmax)) {
-    res = __builtin_nanf("");
-    lse = res;
+    res[0] = res[1] = __builtin_nanf("");
+    lse = res[0];
   } else {
-    const int ns = (L + 1 + kDecodeSplit - 1) / kDecodeSplit;
+    const int ns = (L + 1 + a.split - 1) / a.split;
     const long p0 = ((long)b * a.H + h) * a.nsplit;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[p0 + s].x);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float2 ml = a.part_ml[p0 + s];
-      const float wgt = exp2f(ml.x - M);
-      num = fmaf(wgt, a.part_o[(p0 + s) * HD + d], num);
-      den = fmaf(wgt, ml.y, den);
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_ml[p0 + s].x);
+    M = wave_max(M);
+    float den = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      float w = 0.f;
+      if (s0 + lane < ns) {
+        const float2 ml = a.part_ml[p0 + s0 + lane];
+        w = exp2f(ml.x - M);
+        den = fmaf(w, ml.y, den);
+      }
+      const int cnt = min(64, ns - s0);
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __shfl(w, j);
+        const float* po = a.part_o + (p0 + s0 + j) * HD;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int d = lane + 64 * k;
+          if (d < HD) res[k] = fmaf(wj, po[d], res[k]);
+        }
+      }
     }
-    res = num / den;
+    den = wave_sum(den);
+    res[0] /= den;
+    res[1] /= den;
     lse = (M + log2f(den)) * kLn2;
   }
-  if (a.out_bf16) {
-    reinterpret_cast<uint16_t*>(a.out)[orow + d] = f32_to_bf16_bits(res);
-  } else {
-    reinterpret_cast<float*>(a.out)[orow + d] = res;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int d = lane + 64 * k;
+    if (d >= HD) break;
+    if (a.out_bf16) {
+      reinterpret_cast<uint16_t*>(a.out)[orow + d] = f32_to_bf16_bits(res[k]);
+    } else {
+      reinterpret_cast<float*>(a.out)[orow + d] = res[k];
+    }
   }
-  if (a.lse && d == 0) a.lse[(long)b * a.H + h] = lse;
+  if (a.lse && lane == 0) a.lse[(long)b * a.H + h] = lse;
+}
+
+bool decode_mfma_supported(const DecodeArgs& a, int bf16) {
+  return bf16 && (a.hd == 64 || a.hd == 128) && a.group <= 16;
 }
 
 template <int BF16, int HD>
-hipError_t launch_decode_hd(const DecodeArgs& a, hipStream_t s, const TimingHook& tm) {
+hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHook& tm) {
+  DecodeArgs a = a0;
+  const bool mfma = decode_mfma_supported(a, BF16);
+  a.split = mfma ? kSplitMfma : kDecodeSplit;
+  a.nsplit = (a.Lmax + a.split - 1) / a.split;
+  if (!mfma) a.q_rot = nullptr;
   hipLaunchKernelGGL(decode_append_kernel<BF16>, dim3(a.KV, a.B), dim3(HD / 2), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = tm.before(s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_valu_kernel<BF16, HD>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, s, a);
+  if (mfma) {
+    if constexpr (HD == 64 || HD == 128) {
+      hipLaunchKernelGGL((decode_split_mfma_kernel<HD>), dim3(a.nsplit, a.KV, a.B), dim3(256), 0, s, a);
+    }
+  } else {
+    hipLaunchKernelGGL((decode_split_valu_kernel<BF16, HD>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, s, a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = tm.after(s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<HD>), dim3(a.H, a.B), dim3(HD), 0, s, a);
+  hipLaunchKernelGGL((decode_merge_kernel<HD>), dim3(a.H, a.B), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

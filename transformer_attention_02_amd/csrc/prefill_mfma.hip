@@ -16,11 +16,11 @@
 //   * The key rows fed to the S^T contraction are permuted (bits 2 and 3 of
 //     the row index swapped) so that accumulator registers 8u..8u+7 of a lane
 //     hold 8 consecutive keys: the probabilities then feed O^T = V^T P^T as the
-//     B operand straight from registers (rounded to bf16), and V^T is read from
-//     LDS as 16-byte rows.
+//     B operand straight from registers (rounded to bf16).
 //   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
-//     j+1 are in flight while tile j is computed. V is transposed on its way
-//     into LDS. Both tiles use XOR swizzles so the MFMA operand reads are free
+//     j+1 are in flight while tile j is computed. Both tiles are stored
+//     row-major as loaded; V^T operands are read with ds_read_b64_tr_b16 (the
+//     transposing LDS load of gfx950). XOR swizzles keep the operand reads free
 //     of bank conflicts.
 //   * Causal: tiles past the diagonal are never loaded; a wave skips tiles that
 //     are entirely above its rows; only tiles crossing the diagonal (or the
@@ -38,6 +38,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;  // keys per tile
 constexpr int NW = 4;   // waves per workgroup
@@ -47,10 +48,9 @@ template <int HD>
 struct Cfg {
   static constexpr int KCH = HD / 8;               // 16-byte chunks per key row
   static constexpr int K_BYTES = BN * HD * 2;      // K tile, row-major [key][hd]
-  static constexpr int V_BYTES = HD * BN * 2;      // V^T tile, [hd][key]
+  static constexpr int V_BYTES = BN * HD * 2;      // V tile, row-major [key][hd]
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int K_LOADS = BN * KCH / NT;    // 16-byte K loads per thread
-  static constexpr int V_UNITS = (BN / 4) * KCH;   // (4 keys x 8 dims) V units
+  static constexpr int LOADS = BN * KCH / NT;      // 16-byte loads per thread per tensor
 };
 
 struct GridMap {
@@ -72,8 +72,17 @@ __device__ __forceinline__ int k_off(int r, int c) {
   }
 }
 
-// Byte offset of 16-byte chunk `c` (8 keys) of row `d` of the V^T tile.
-__device__ __forceinline__ int v_off(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
+// Byte offset of 16-byte chunk `c` of key row `r` in the row-major V tile. The
+// XOR spreads the 4-row x 64-byte blocks that one transposing load instruction
+// touches (rows r..r+3, one 32-column slice) over all LDS banks.
+template <int HD>
+__device__ __forceinline__ int v_off(int r, int c) {
+  if constexpr (HD == 128) {
+    return r * 256 + ((c ^ ((r & 3) << 2)) << 4);
+  } else {
+    return r * 128 + ((c ^ (((r >> 1) & 1) << 2)) << 4);
+  }
+}
 
 // Swap bits 2 and 3 of a row index in [0, 32).
 __device__ __forceinline__ int perm_row(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -88,54 +97,35 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
 
 // Registers holding one K/V tile between its global load and its LDS store.
-// Thread t loads K chunks e = t + 256 i (row e / KCH, chunk e % KCH) and, if it
-// owns a V unit, 4 consecutive keys x 8 dims that it writes transposed.
+// Thread t moves chunks e = t + 256 i (key row e / KCH, 16-byte chunk e % KCH)
+// of both tensors; every wave instruction covers whole rows, so the global
+// loads are fully coalesced and the LDS stores are conflict-free.
 template <int HD>
 struct Stage {
   using C = Cfg<HD>;
-  uint4 k[C::K_LOADS];
-  uint4 v0, v1, v2, v3;
+  uint4 k[C::LOADS];
+  uint4 v[C::LOADS];
 
-  __device__ __forceinline__ void load(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, int tid, int vkg,
-                                       int vch, bool v_thread) {
+  __device__ __forceinline__ void load(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, int tid) {
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
+    for (int i = 0; i < C::LOADS; ++i) {
       const int e = tid + NT * i;
       const int r = e / C::KCH, c = e % C::KCH;
       const int key = kt * BN + r;
-      k[i] = key < T ? *reinterpret_cast<const uint4*>(Kg + (long)key * HD + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-    if (v_thread) {
-      const int key = kt * BN + 4 * vkg;
-      const uint16_t* p = Vg + (long)key * HD + vch * 8;
-      v0 = key + 0 < T ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-      v1 = key + 1 < T ? *reinterpret_cast<const uint4*>(p + HD) : make_uint4(0, 0, 0, 0);
-      v2 = key + 2 < T ? *reinterpret_cast<const uint4*>(p + 2 * HD) : make_uint4(0, 0, 0, 0);
-      v3 = key + 3 < T ? *reinterpret_cast<const uint4*>(p + 3 * HD) : make_uint4(0, 0, 0, 0);
+      const long off = (long)key * HD + c * 8;
+      k[i] = key < T ? *reinterpret_cast<const uint4*>(Kg + off) : make_uint4(0, 0, 0, 0);
+      v[i] = key < T ? *reinterpret_cast<const uint4*>(Vg + off) : make_uint4(0, 0, 0, 0);
     }
   }
 
-  __device__ __forceinline__ void store(unsigned char* kb, int tid, int vkg, int vch, bool v_thread) const {
+  __device__ __forceinline__ void store(unsigned char* kb, int tid) const {
     unsigned char* vb = kb + C::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
+    for (int i = 0; i < C::LOADS; ++i) {
       const int e = tid + NT * i;
       const int r = e / C::KCH, c = e % C::KCH;
       *reinterpret_cast<uint4*>(kb + k_off<HD>(r, c)) = k[i];
-    }
-    if (v_thread) {
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const int d = vch * 8 + 2 * wd;
-        const uint32_t w0 = comp(v0, wd), w1 = comp(v1, wd), w2 = comp(v2, wd), w3 = comp(v3, wd);
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-        *reinterpret_cast<uint2*>(vb + v_off(d, vkg >> 1) + (vkg & 1) * 8) = lo;
-        *reinterpret_cast<uint2*>(vb + v_off(d + 1, vkg >> 1) + (vkg & 1) * 8) = hi;
-      }
+      *reinterpret_cast<uint4*>(vb + v_off<HD>(r, c)) = v[i];
     }
   }
 };
@@ -208,12 +198,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int nkt = a.causal ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
 
   // ---- global -> registers -> LDS staging
-  const int vkg = tid & 15;  // key group (4 keys) of this thread's V unit
-  const int vch = tid >> 4;  // 8-dim chunk of this thread's V unit
-  const bool v_thread = tid < C::V_UNITS;
   Stage<HD> st;
-  st.load(Kg, Vg, 0, a.T, tid, vkg, vch, v_thread);
-  st.store(smem, tid, vkg, vch, v_thread);
+  st.load(Kg, Vg, 0, a.T, tid);
+  st.store(smem, tid);
   __syncthreads();
 
   f32x16 oacc[HD / 32];
@@ -226,7 +213,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int stage = kt & 1;
-    if (kt + 1 < nkt) st.load(Kg, Vg, kt + 1, a.T, tid, vkg, vch, v_thread);
+    if (kt + 1 < nkt) st.load(Kg, Vg, kt + 1, a.T, tid);
     const int k0 = kt * BN;
     const bool skip = !wave_active || (a.causal && k0 > qw0 + 31);
     if (!skip) {
@@ -288,14 +275,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         pw.z = pack_bf16x2(t[8 * u + 4], t[8 * u + 5]);
         pw.w = pack_bf16x2(t[8 * u + 6], t[8 * u + 7]);
         const bf16x8 pb = as_bf16x8(pw);
+        // V^T operand through transposing loads: source lane i of a 16-lane group
+        // points at key row 16u + 8hf + i/4 (+4), columns d0 + 4*(i%4); lane i
+        // then holds V[those 4 keys][d0 + i].
 #pragma unroll
         for (int mb = 0; mb < HD / 32; ++mb) {
-          const uint4 av = *reinterpret_cast<const uint4*>(vb + v_off(32 * mb + n, 2 * u + hf));
-          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pb, oacc[mb], 0, 0, 0);
+          const int li = lane & 15;
+          const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+          const int r = 16 * u + 8 * hf + (li >> 2);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r, col >> 3) + (col & 7) * 2));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r + 4, col >> 3) + (col & 7) * 2));
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[mb], 0, 0, 0);
         }
       }
     }
-    if (kt + 1 < nkt) st.store(smem + (stage ^ 1) * C::STAGE, tid, vkg, vch, v_thread);
+    if (kt + 1 < nkt) st.store(smem + (stage ^ 1) * C::STAGE, tid);
     __syncthreads();
   }
 

@@ -21,28 +21,53 @@ __device__ __forceinline__ float ld(const void* base, long i) {
   }
 }
 
-// Rotate every key row once: row r = (b, g, t) sits at position pos0 + t.
-// One thread per interleaved pair (2p, 2p+1); angle (pos0 + t) * theta_p.
-// Output keeps the input element type (bf16 outputs are rounded to nearest even,
-// exactly as the MFMA kernel would round a rotated tile before its contraction).
+// Rotate every key row once: row (b, g) token t sits at position pos0 + t.
+// A thread owns one (token, 16-byte chunk) and rotates that chunk in kRopeRows
+// consecutive (b, g) rows, so the cos/sin of its pairs are computed once and
+// reused; all loads are issued before the stores. Output keeps the input type
+// (bf16 rounded to nearest even, exactly as a rotated tile would be rounded
+// before an MFMA contraction).
+constexpr int kRopeRows = 8;
+
 template <int BF16>
 __global__ __launch_bounds__(256) void rope_k_kernel(RopeKArgs a) {
-  const int half = a.hd >> 1;
-  const long pair = (long)blockIdx.x * 256 + threadIdx.x;
-  if (pair >= a.rows * half) return;
-  const long row = pair / half;
-  const int p = (int)(pair - row * half);
-  const int t = (int)(row % a.T);
-  float c, s;
-  rope_cos_sin(a.pos0 + t, a.freqs.rev[p], c, s);
-  const long e = row * a.hd + 2 * p;
-  if constexpr (BF16) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(a.k)[e >> 1];
-    const float x0 = bf16_bits_to_f32(w & 0xffffu), x1 = bf16_bits_to_f32(w >> 16);
-    reinterpret_cast<uint32_t*>(a.kr)[e >> 1] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
-  } else {
-    const float2 w = reinterpret_cast<const float2*>(a.k)[e >> 1];
-    reinterpret_cast<float2*>(a.kr)[e >> 1] = make_float2(w.x * c - w.y * s, w.x * s + w.y * c);
+  constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int chunks = a.hd / EPC;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)a.T * chunks) return;
+  const int t = (int)(idx / chunks), c = (int)(idx % chunks);
+  float cs[EPC / 2], sn[EPC / 2];
+#pragma unroll
+  for (int p = 0; p < EPC / 2; ++p) rope_cos_sin(a.pos0 + t, a.freqs.rev[c * (EPC / 2) + p], cs[p], sn[p]);
+  const int r0 = blockIdx.y * kRopeRows;
+  const uint4* __restrict__ src = reinterpret_cast<const uint4*>(a.k);
+  uint4* __restrict__ dst = reinterpret_cast<uint4*>(a.kr);
+  uint4 x[kRopeRows];
+#pragma unroll
+  for (int j = 0; j < kRopeRows; ++j) {
+    const long e = (((long)(r0 + j) * a.T + t) * a.hd + (long)c * EPC) / EPC;
+    x[j] = (r0 + j < a.heads) ? src[e] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kRopeRows; ++j) {
+    if (r0 + j >= a.heads) break;
+    const long e = (((long)(r0 + j) * a.T + t) * a.hd + (long)c * EPC) / EPC;
+    uint4 y;
+    if constexpr (BF16) {
+      uint32_t w[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = bf16_bits_to_f32(w[p] & 0xffffu), x1 = bf16_bits_to_f32(w[p] >> 16);
+        w[p] = pack_bf16x2(x0 * cs[p] - x1 * sn[p], x0 * sn[p] + x1 * cs[p]);
+      }
+      y = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      const float f0 = __uint_as_float(x[j].x), f1 = __uint_as_float(x[j].y);
+      const float f2 = __uint_as_float(x[j].z), f3 = __uint_as_float(x[j].w);
+      y = make_uint4(__float_as_uint(f0 * cs[0] - f1 * sn[0]), __float_as_uint(f0 * sn[0] + f1 * cs[0]),
+                     __float_as_uint(f2 * cs[1] - f3 * sn[1]), __float_as_uint(f2 * sn[1] + f3 * cs[1]));
+    }
+    dst[e] = y;
   }
 }
 
@@ -157,8 +182,8 @@ hipError_t launch_valu_hd(const PrefillArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_rope_k(const RopeKArgs& a, int bf16, hipStream_t s) {
-  const long pairs = a.rows * (a.hd / 2);
-  dim3 grid((unsigned)((pairs + 255) / 256));
+  const long items = (long)a.T * (a.hd / (bf16 ? 8 : 4));
+  dim3 grid((unsigned)((items + 255) / 256), (unsigned)((a.heads + kRopeRows - 1) / kRopeRows));
   if (bf16) {
     hipLaunchKernelGGL(rope_k_kernel<1>, grid, dim3(256), 0, s, a);
   } else {
