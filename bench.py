@@ -210,7 +210,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="all", choices=["all", "prefill", "decode", "alibi", "small"])
+    ap.add_argument("--workload", default="all", choices=["all", "prefill", "decode", "alibi", "small", "copy"],
+                    help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--cpu-seqs", type=int, default=8)
@@ -232,6 +233,24 @@ def main():
     bd.load()
     dev = torch.device("cuda:0")
     hip = HipEvents()
+
+    if args.workload == "copy":
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        nbytes = 2 * src.numel() * src.element_size()
+        print(json.dumps({"workload": "copy", "bytes_read": nbytes // 2, "bytes_written": nbytes // 2,
+                          "ms": ms, "GB/s": nbytes / ms / 1e6}), flush=True)
+        return
 
     pre_w = {"all": W.LLAMA3_8B, "prefill": W.LLAMA3_8B, "alibi": W.ALIBI_MHA, "small": W.SMALL_BF16}.get(args.workload)
     pre = Prefill(pre_w, dev, bd, W, torch) if pre_w is not None else None

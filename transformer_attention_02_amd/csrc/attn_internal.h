@@ -87,9 +87,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // round to nearest even
 }
 
-// Two floats -> two bf16 packed in one dword (low half = lo), round to nearest even.
+// Two floats -> two bf16 packed in one dword (low half = lo), round to nearest
+// even, with one v_cvt_pk_bf16_f32.
+typedef float attn_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 attn_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  const attn_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, attn_bf16x2));
+}
+
+// Raw buffer descriptor over [base, base + bytes) (gfx9-family word 3). Buffer
+// loads through it return zero for any lane whose offset is at or past `bytes`,
+// so a descriptor that starts at a tile and ends at the end of the tensor slab
+// zero-fills rows past the sequence end without per-lane address checks.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
 }
 
 // cos/sin of the rotary angle pos * theta, with q4 = 4 * theta / (2 pi) in fp64

@@ -376,13 +376,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
         den = fmaf(w, ml.y, den);
       }
       const int cnt = min(64, ns - s0);
-      for (int j = 0; j < cnt; ++j) {
-        const float wj = __shfl(w, j);
-        const float* po = a.part_o + (p0 + s0 + j) * HD;
+      // 8 splits per step with all loads issued before the multiply-adds
+      for (int j0 = 0; j0 < cnt; j0 += 8) {
+        float v[8][2];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int d = lane + 64 * k;
-          if (d < HD) res[k] = fmaf(wj, po[d], res[k]);
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int d = lane + 64 * k;
+            v[u][k] = (j0 + u < cnt && d < HD) ? a.part_o[(p0 + s0 + j0 + u) * HD + d] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wj = __shfl(w, j0 + u);
+          res[0] = fmaf(wj, v[u][0], res[0]);
+          res[1] = fmaf(wj, v[u][1], res[1]);
         }
       }
     }

@@ -106,15 +106,17 @@ struct Stage {
   uint4 k[C::LOADS];
   uint4 v[C::LOADS];
 
+  // Loads tile kt through buffer descriptors that start at the tile and end at
+  // the slab end: rows at or past T read as zero.
   __device__ __forceinline__ void load(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, int tid) {
+    const int bytes = (T - kt * BN) * HD * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)kt * BN * HD, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)kt * BN * HD, bytes);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int e = tid + NT * i;
-      const int r = e / C::KCH, c = e % C::KCH;
-      const int key = kt * BN + r;
-      const long off = (long)key * HD + c * 8;
-      k[i] = key < T ? *reinterpret_cast<const uint4*>(Kg + off) : make_uint4(0, 0, 0, 0);
-      v[i] = key < T ? *reinterpret_cast<const uint4*>(Vg + off) : make_uint4(0, 0, 0, 0);
+      const int e = tid + NT * i;  // row e / KCH, chunk e % KCH: byte offset 16 e
+      k[i] = buffer_load16(rk, 16 * e);
+      v[i] = buffer_load16(rv, 16 * e);
     }
   }
 
@@ -130,7 +132,117 @@ struct Stage {
   }
 };
 
-template <int HD>
+// One wave's online-softmax state over its 32 query rows, and the work of one
+// 64-key tile. MASK selects the variant for tiles that cross the causal
+// diagonal or the sequence end; every other tile runs without masking code.
+template <int HD, bool ALIBI, bool CAUSAL>
+struct WaveState {
+  f32x16 oacc[HD / 32];  // O^T: lane holds query n, dims 32mb + 8(r/4) + 4hf + r%4
+  bf16x8 qf[HD / 16];    // Q^T B operand, k-step s: dims 16s + 8hf .. +7
+  float m_run;           // running max (log2 units), per row
+  float l_run;           // this half-wave's part of the running denominator
+  float c2;              // log2(e) / sqrt(hd)
+  float slope2;          // ALiBi slope * log2(e)
+  int qi;                // this lane's query row
+  int T;
+  int lane;
+
+  template <bool MASK>
+  __device__ __forceinline__ void tile(const unsigned char* kb, int k0) {
+    using C = Cfg<HD>;
+    const unsigned char* vb = kb + C::K_BYTES;
+    const int n = lane & 31, hf = lane >> 5;
+    // S^T = K Q^T; the K rows are read in permuted order (perm_row) so that
+    // register i of the two accumulators holds key k0 + 32(i/16) + 16((i%16)/8) + 8hf + i%8.
+    f32x16 sacc[2];
+    const int krow = perm_row(n);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      sacc[kb2] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < HD / 16; ++s) {
+        const uint4 av = *reinterpret_cast<const uint4*>(kb + k_off<HD>(32 * kb2 + krow, 2 * s + hf));
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), qf[s], sacc[kb2], 0, 0, 0);
+      }
+    }
+    // Without ALiBi t keeps the raw scores (the max commutes with the positive
+    // scale, which is folded into the exponent's FMA); with ALiBi t is the
+    // scaled, biased score in log2 units.
+    float t[32];
+    const int dbase = k0 + 8 * hf - qi;  // key - query at register offset 0
+    if constexpr (ALIBI) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float dk = (float)(dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8));
+        t[i] = fmaf(sacc[i / 16][i % 16], c2, slope2 * (CAUSAL ? dk : -fabsf(dk)));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) t[i] = sacc[i / 16][i % 16];
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int dk = dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
+        const bool vis = (dk + qi < T) && (!CAUSAL || dk <= 0);
+        t[i] = vis ? t[i] : -INFINITY;
+      }
+    }
+    float mx = t[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, t[i]);
+    mx = fmaxf(mx, xhalf(mx));
+    const float ms = ALIBI ? mx : mx * c2;  // tile max in log2 units
+    // Lazy rescale: a row's running max only moves when its tile max exceeds
+    // it by more than 8 (a factor 2^8); otherwise the stale max is kept for
+    // both the numerator and the denominator, which leaves O / l unchanged.
+    // The decision is per row (a row that does not move multiplies by exactly
+    // 1), so no row's arithmetic depends on another row's scores; the
+    // wave-wide test only skips the multiplies when no row moves.
+    const bool move = ms > m_run + 8.0f;
+    if (__any(move)) {
+      // (a side effect keeps this a real branch: the compiler would otherwise
+      // hoist the multiplies, which are an identity when no row moves)
+      asm volatile("; rescale" ::: "memory");
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - ms) : 1.0f;
+      m_run = move ? ms : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < HD / 32; ++mb) oacc[mb] *= alpha;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      t[i] = __builtin_amdgcn_exp2f(ALIBI ? t[i] - m_run : fmaf(t[i], c2, -m_run));
+      lsum += t[i];
+    }
+    l_run += lsum;
+    // O^T += V^T P^T over four 16-key steps. P^T (the B operand) comes straight
+    // from t[8u .. 8u+7]; V^T is read with transposing loads: source lane i of a
+    // 16-lane group points at key row 16u + 8hf + i/4 (+4), columns d0 + 4(i%4),
+    // and lane i then holds V[those 4 keys][d0 + i].
+    const int li = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 pw = make_uint4(pack_bf16x2(t[8 * u + 0], t[8 * u + 1]), pack_bf16x2(t[8 * u + 2], t[8 * u + 3]),
+                                  pack_bf16x2(t[8 * u + 4], t[8 * u + 5]), pack_bf16x2(t[8 * u + 6], t[8 * u + 7]));
+      const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+      for (int mb = 0; mb < HD / 32; ++mb) {
+        const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+        const int r = 16 * u + 8 * hf + (li >> 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r, col >> 3) + (col & 7) * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r + 4, col >> 3) + (col & 7) * 2));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[mb], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <int HD, bool ALIBI, bool CAUSAL, bool OUT_BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using C = Cfg<HD>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
@@ -162,142 +274,95 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int head = kvh * a.group + hc * gm.hpw + (wave % gm.hpw);
   const int q0 = qb * gm.bm;
   const int qw0 = q0 + 32 * (wave / gm.hpw);
-  const int qi = qw0 + n;
   const bool wave_active = qw0 < a.T;
-
-  // ---- Q rows -> B operand (rotated in fp32, rounded to bf16)
-  bf16x8 qf[HD / 16];
-  {
-    const int qrow = min(qi, a.T - 1);
-    const uint4* src =
-        reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + (((long)b * a.H + head) * a.T + qrow) * HD);
-#pragma unroll
-    for (int s = 0; s < HD / 16; ++s) {
-      const uint4 wv = src[2 * s + hf];
-      if (a.rope) {
-        uint32_t d[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          float c, sn;
-          rope_cos_sin(a.pos0 + qi, a.freqs.rev[8 * s + 4 * hf + p], c, sn);
-          const uint32_t x = comp(wv, p);
-          const float x0 = bf16_bits_to_f32(x & 0xffffu), x1 = bf16_bits_to_f32(x >> 16);
-          d[p] = pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
-        }
-        qf[s] = as_bf16x8(make_uint4(d[0], d[1], d[2], d[3]));
-      } else {
-        qf[s] = as_bf16x8(wv);
-      }
-    }
-  }
 
   const long kvoff = ((long)b * a.KV + kvh) * (long)a.T * HD;
   const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k) + kvoff;
   const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v) + kvoff;
   const int q_last = min(a.T, q0 + gm.bm) - 1;
-  const int nkt = a.causal ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
+  const int nkt = CAUSAL ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
 
-  // ---- global -> registers -> LDS staging
+  // The first K/V tile's global loads are in flight during the Q set-up.
   Stage<HD> st;
   st.load(Kg, Vg, 0, a.T, tid);
+
+  WaveState<HD, ALIBI, CAUSAL> ws;
+  ws.qi = qw0 + n;
+  ws.T = a.T;
+  ws.lane = lane;
+  ws.c2 = a.scale_log2;
+  ws.slope2 = ALIBI ? alibi_slope(a.alibi, head, a.H) * 1.4426950408889634f : 0.f;
+  ws.m_run = -INFINITY;
+  ws.l_run = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < HD / 32; ++mb) ws.oacc[mb] = f32x16{};
+
+  // ---- Q rows -> B operand (rotated in fp32, rounded to bf16). The rotary
+  // cos/sin of the workgroup's bm rows are computed once into LDS (layout
+  // [pair][row], so lanes reading consecutive rows hit distinct banks) and
+  // shared by the waves of all heads in the workgroup.
+  {
+    const int qrow = min(ws.qi, a.T - 1);
+    const uint4* src =
+        reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + (((long)b * a.H + head) * a.T + qrow) * HD);
+    uint4 qraw[HD / 16];
+#pragma unroll
+    for (int s = 0; s < HD / 16; ++s) qraw[s] = src[2 * s + hf];
+    if (a.rope) {
+      float2* cs = reinterpret_cast<float2*>(smem);  // [HD/2][bm]
+      for (int e = tid; e < (HD / 2) * gm.bm; e += NT) {
+        const int r = e % gm.bm, p = e / gm.bm;
+        float c, sn;
+        rope_cos_sin(a.pos0 + q0 + r, a.freqs.rev[p], c, sn);
+        cs[e] = make_float2(c, sn);
+      }
+      __syncthreads();
+      const int r = ws.qi - q0;
+#pragma unroll
+      for (int s = 0; s < HD / 16; ++s) {
+        uint32_t d[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float2 t = cs[(8 * s + 4 * hf + p) * gm.bm + r];
+          const uint32_t x = comp(qraw[s], p);
+          const float x0 = bf16_bits_to_f32(x & 0xffffu), x1 = bf16_bits_to_f32(x >> 16);
+          d[p] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+        }
+        ws.qf[s] = as_bf16x8(make_uint4(d[0], d[1], d[2], d[3]));
+      }
+      __syncthreads();  // the table area is reused by the K/V tiles
+    } else {
+#pragma unroll
+      for (int s = 0; s < HD / 16; ++s) ws.qf[s] = as_bf16x8(qraw[s]);
+    }
+  }
+
   st.store(smem, tid);
   __syncthreads();
 
-  f32x16 oacc[HD / 32];
-#pragma unroll
-  for (int mb = 0; mb < HD / 32; ++mb) oacc[mb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = a.scale_log2;
-  const float slope2 = a.alibi ? alibi_slope(a.alibi, head, a.H) * 1.4426950408889634f : 0.f;
-  const int krow0 = perm_row(n);
-
-  for (int kt = 0; kt < nkt; ++kt) {
+  // Tiles [0, kt_clean) need no mask for any row of the workgroup: every key is
+  // at or before the first query row (causal) and inside the sequence.
+  const int kt_clean = min(nkt, CAUSAL ? min((q0 + 1) / BN, a.T / BN) : a.T / BN);
+  int kt = 0;
+  for (; kt < kt_clean; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < nkt) st.load(Kg, Vg, kt + 1, a.T, tid);
+    if (wave_active) ws.template tile<false>(smem + stage * C::STAGE, kt * BN);
+    if (kt + 1 < nkt) st.store(smem + (stage ^ 1) * C::STAGE, tid);
+    __syncthreads();
+  }
+  for (; kt < nkt; ++kt) {
     const int stage = kt & 1;
     if (kt + 1 < nkt) st.load(Kg, Vg, kt + 1, a.T, tid);
     const int k0 = kt * BN;
-    const bool skip = !wave_active || (a.causal && k0 > qw0 + 31);
-    if (!skip) {
-      const unsigned char* kb = smem + stage * C::STAGE;
-      const unsigned char* vb = kb + C::K_BYTES;
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        sacc[kb2] = f32x16{};
-        const int r = 32 * kb2 + krow0;
-#pragma unroll
-        for (int s = 0; s < HD / 16; ++s) {
-          const uint4 av = *reinterpret_cast<const uint4*>(kb + k_off<HD>(r, 2 * s + hf));
-          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), qf[s], sacc[kb2], 0, 0, 0);
-        }
-      }
-      // scores in log2 units; register i of t[] holds key k0 + 32*(i/16) + 16*((i%16)/8) + 8*hf + i%8
-      float t[32];
-      const bool edge = (a.causal && k0 + BN - 1 > qw0) || (k0 + BN > a.T);
-      const int dbase = k0 + 8 * hf - qi;  // key - query for register offset 0
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int koff = 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
-        float x = sacc[i / 16][i % 16];
-        if (a.alibi) {
-          const float dk = (float)(dbase + koff);
-          x = fmaf(x, c2, slope2 * (a.causal ? dk : -fabsf(dk)));
-        } else {
-          x *= c2;
-        }
-        if (edge) {
-          const int key = k0 + 8 * hf + koff;
-          const bool vis = key < a.T && (!a.causal || key <= qi);
-          x = vis ? x : -INFINITY;
-        }
-        t[i] = x;
-      }
-      float mx = t[0];
-#pragma unroll
-      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, t[i]);
-      mx = fmaxf(mx, xhalf(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        t[i] = __builtin_amdgcn_exp2f(t[i] - m_new);
-        lsum += t[i];
-      }
-      l_run = fmaf(l_run, alpha, lsum);
-      m_run = m_new;
-#pragma unroll
-      for (int mb = 0; mb < HD / 32; ++mb) oacc[mb] *= alpha;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint4 pw;
-        pw.x = pack_bf16x2(t[8 * u + 0], t[8 * u + 1]);
-        pw.y = pack_bf16x2(t[8 * u + 2], t[8 * u + 3]);
-        pw.z = pack_bf16x2(t[8 * u + 4], t[8 * u + 5]);
-        pw.w = pack_bf16x2(t[8 * u + 6], t[8 * u + 7]);
-        const bf16x8 pb = as_bf16x8(pw);
-        // V^T operand through transposing loads: source lane i of a 16-lane group
-        // points at key row 16u + 8hf + i/4 (+4), columns d0 + 4*(i%4); lane i
-        // then holds V[those 4 keys][d0 + i].
-#pragma unroll
-        for (int mb = 0; mb < HD / 32; ++mb) {
-          const int li = lane & 15;
-          const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-          const int r = 16 * u + 8 * hf + (li >> 2);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r, col >> 3) + (col & 7) * 2));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r + 4, col >> 3) + (col & 7) * 2));
-          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[mb], 0, 0, 0);
-        }
-      }
-    }
+    if (wave_active && !(CAUSAL && k0 > qw0 + 31)) ws.template tile<true>(smem + stage * C::STAGE, k0);
     if (kt + 1 < nkt) st.store(smem + (stage ^ 1) * C::STAGE, tid);
     __syncthreads();
   }
 
   if (!wave_active) return;
-  const float l_tot = l_run + xhalf(l_run);
+  const float l_tot = ws.l_run + xhalf(ws.l_run);
+  const int qi = ws.qi;
   if (qi >= a.T) return;
   const float inv_l = 1.0f / l_tot;
   const long orow = (((long)b * a.H + head) * a.T + qi) * HD;
@@ -306,9 +371,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = 32 * mb + 8 * g4 + 4 * hf;
-      const float o0 = oacc[mb][4 * g4 + 0] * inv_l, o1 = oacc[mb][4 * g4 + 1] * inv_l;
-      const float o2 = oacc[mb][4 * g4 + 2] * inv_l, o3 = oacc[mb][4 * g4 + 3] * inv_l;
-      if (a.out_bf16) {
+      const float o0 = ws.oacc[mb][4 * g4 + 0] * inv_l, o1 = ws.oacc[mb][4 * g4 + 1] * inv_l;
+      const float o2 = ws.oacc[mb][4 * g4 + 2] * inv_l, o3 = ws.oacc[mb][4 * g4 + 3] * inv_l;
+      if constexpr (OUT_BF16) {
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d) =
             make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
       } else {
@@ -316,7 +381,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     }
   }
-  if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.T + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+  if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.T + qi] = (ws.m_run + log2f(l_tot)) * 0.69314718055994531f;
 }
 
 GridMap make_grid(const PrefillArgs& a) {
@@ -330,10 +395,31 @@ GridMap make_grid(const PrefillArgs& a) {
   return gm;
 }
 
+template <int HD, bool ALIBI, bool CAUSAL>
+void launch_out(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
+  if (a.out_bf16) {
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, true>), grid, dim3(NT), 0, s, a, gm);
+  } else {
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, false>), grid, dim3(NT), 0, s, a, gm);
+  }
+}
+
+template <int HD>
+void launch_hd(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
+  if (a.alibi) {
+    if (a.causal) launch_out<HD, true, true>(a, gm, grid, s);
+    else launch_out<HD, true, false>(a, gm, grid, s);
+  } else {
+    if (a.causal) launch_out<HD, false, true>(a, gm, grid, s);
+    else launch_out<HD, false, false>(a, gm, grid, s);
+  }
+}
+
 }  // namespace
 
 bool prefill_mfma_supported(const PrefillArgs& a, int bf16) {
   if (!bf16 || (a.hd != 64 && a.hd != 128)) return false;
+  if ((long)a.T * a.hd * 2 >= (1L << 31)) return false;  // buffer descriptors hold 32-bit sizes
   const GridMap gm = make_grid(a);
   return (long)gm.units * gm.nqb < (1L << 31);
 }
@@ -342,9 +428,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
   const GridMap gm = make_grid(a);
   const dim3 grid((unsigned)(gm.units * gm.nqb));
   if (a.hd == 128) {
-    hipLaunchKernelGGL(prefill_mfma_kernel<128>, grid, dim3(NT), 0, s, a, gm);
+    launch_hd<128>(a, gm, grid, s);
   } else {
-    hipLaunchKernelGGL(prefill_mfma_kernel<64>, grid, dim3(NT), 0, s, a, gm);
+    launch_hd<64>(a, gm, grid, s);
   }
   return hipGetLastError();
 }
