@@ -182,17 +182,16 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
 
 namespace {
 // Workspace layout (sized for the smaller split, so it fits either kernel):
-// [part_o: rows*hd fp32][part_ml: rows float2][q_rot: B*H*hd bf16], rows = B*H*ceil(Lmax/256).
+// [part_o: rows*hd fp32][part_ml: rows float2], rows = B*H*ceil(Lmax/256).
 struct DecodeWs {
-  long long part_o, part_ml, q_rot, total;
+  long long part_o, part_ml, total;
 };
 DecodeWs decode_ws_layout(int B, int H, int hd, int Lmax) {
   const long long rows = (long long)B * H * ((Lmax + kDecodeSplit - 1) / kDecodeSplit);
   DecodeWs w;
   w.part_o = 0;
   w.part_ml = rows * hd * 4;
-  w.q_rot = (w.part_ml + rows * 8 + 255) / 256 * 256;
-  w.total = (w.q_rot + (long long)B * H * hd * 2 + 255) / 256 * 256;
+  w.total = (w.part_ml + rows * 8 + 255) / 256 * 256;
   return w;
 }
 }  // namespace
@@ -244,7 +243,6 @@ int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k
   char* ws = reinterpret_cast<char*>(workspace);
   a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   a.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
-  a.q_rot = reinterpret_cast<uint16_t*>(ws + lay.q_rot);
   a.split = kDecodeSplit;  // the launcher sets the split of the kernel it picks
   a.nsplit = (Lmax + kDecodeSplit - 1) / kDecodeSplit;
   a.rope = rope_base != 0.0;

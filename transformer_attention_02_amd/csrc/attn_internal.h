@@ -54,7 +54,6 @@ struct DecodeArgs {
   float* lse;            // [B,H] or nullptr
   float* part_o;         // [B,H,nsplit,hd]
   float2* part_ml;       // [B,H,nsplit]  (running max in log2 units, denominator)
-  uint16_t* q_rot;       // [B,H,hd] bf16 query rotated at L (MFMA path)
   int B, H, KV, hd, group, Lmax;
   int split;             // key slots per partial
   int nsplit;            // partial slots per (b, h): ceil(Lmax / split)

@@ -30,8 +30,8 @@ __device__ __forceinline__ float ld(const void* base, long i) {
 __device__ __forceinline__ bool bad_len(int L, int Lmax) { return L < 0 || L >= Lmax; }
 
 // Grid (KV, B), hd/2 threads (one interleaved pair each): rotate k_new at L and
-// write slot L of both caches; for the MFMA path also rotate the group's query
-// heads at L (same cos/sin) into q_rot as bf16.
+// write slot L of both caches (vector-ALU path; the MFMA split kernel does this
+// itself).
 template <int BF16>
 __global__ void decode_append_kernel(DecodeArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, p = threadIdx.x;
@@ -46,13 +46,6 @@ __global__ void decode_append_kernel(DecodeArgs a) {
   if constexpr (BF16) {
     reinterpret_cast<uint32_t*>(a.k_cache)[dst >> 1] = pack_bf16x2(y0, y1);
     reinterpret_cast<uint32_t*>(a.v_cache)[dst >> 1] = reinterpret_cast<const uint32_t*>(a.v_new)[src >> 1];
-    if (a.q_rot) {
-      for (int j = 0; j < a.group; ++j) {
-        const long qi = ((long)b * a.H + g * a.group + j) * a.hd + 2 * p;
-        const float q0 = ld<BF16>(a.q, qi), q1 = ld<BF16>(a.q, qi + 1);
-        reinterpret_cast<uint32_t*>(a.q_rot)[qi >> 1] = pack_bf16x2(q0 * c - q1 * s, q0 * s + q1 * c);
-      }
-    }
   } else {
     reinterpret_cast<float2*>(a.k_cache)[dst >> 1] = make_float2(y0, y1);
     reinterpret_cast<float2*>(a.v_cache)[dst >> 1] = reinterpret_cast<const float2*>(a.v_new)[src >> 1];
@@ -134,7 +127,7 @@ __global__ __launch_bounds__(256) void decode_split_valu_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- MFMA split kernel
-// bf16, hd in {64, 128}, group = H/KV <= 16. Grid (nsplit, KV, B), 4 waves,
+// bf16, hd in {64, 128}, group = H/KV <= 16. Grid (KV*B, nsplit), 4 waves,
 // kSplitMfma key slots per workgroup.
 // The group's query heads are the columns of S^T = K Q^T computed with
 // v_mfma_f32_16x16x32_bf16, so each K/V byte is read from memory once for all of
@@ -145,9 +138,10 @@ __global__ __launch_bounds__(256) void decode_split_valu_kernel(DecodeArgs a) {
 // with an XOR swizzle and read as V^T with ds_read_b64_tr_b16, the transposing
 // LDS load of gfx950. Key rows are permuted so that a lane's accumulator
 // registers hold 8 consecutive keys, which feed O^T = V^T P^T as its B operand
-// straight from registers. The query arrives rotated (the append kernel rotates
-// it once per head). The four waves' (m, l, O) are merged in LDS and one partial
-// per head is written.
+// straight from registers. Each workgroup rotates the query with a cos/sin table
+// for position L in LDS; the workgroup whose split holds slot L also appends the
+// new key/value (cache write plus an LDS patch of its own tile). The four waves'
+// (m, l, O) are merged in LDS and one partial per head is written.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -186,7 +180,10 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ float mer_m[kWaves][16];
   __shared__ float mer_l[kWaves][16];
 
-  const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // Grid (KV*B, nsplit): every sequence's first split is dispatched before any
+  // second split, so the blocks past a short sequence's end (which exit at once)
+  // cluster at the end of the dispatch order.
+  const int sp = blockIdx.y, kvh = blockIdx.x % a.KV, b = blockIdx.x / a.KV;
   const int L = a.lens[b];
   if (bad_len(L, a.Lmax)) return;
   const int nk = L + 1;
@@ -198,13 +195,52 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   const bool qcol = n < G;
   const int head = kvh * G + (qcol ? n : 0);
 
-  // Q^T B operand (rotated at L by the append kernel): column n, k-step s -> dims 32s + 8g .. +7
+  // cos/sin of the rotary angle at position L for every pair, shared in LDS.
+  __shared__ float2 cs_tab[HD / 2];
+  if (tid < HD / 2) {
+    float c = 1.f, sn = 0.f;
+    if (a.rope) rope_cos_sin(L, a.freqs.rev[tid], c, sn);
+    cs_tab[tid] = make_float2(c, sn);
+  }
+  // This split holds the new token's slot L: its workgroup writes the rotated
+  // key and the value to the cache, and the wave whose tile covers slot L
+  // patches that row of its LDS tile (it never reads slot L back from memory).
+  const bool own_slot = L >= k0 && L < k0 + kSplitMfma;
+  uint32_t knew = 0, vnew = 0;  // lane p < HD/2: pair p of R(L) k_new and v_new (bf16x2)
+  const long cslot = (((long)b * a.KV + kvh) * a.Lmax + L) * HD;
+  const long nslot = ((long)b * a.KV + kvh) * HD;
+  __syncthreads();
+  if (own_slot && lane < HD / 2) {
+    const uint32_t kw = reinterpret_cast<const uint32_t*>(a.k_new)[(nslot >> 1) + lane];
+    vnew = reinterpret_cast<const uint32_t*>(a.v_new)[(nslot >> 1) + lane];
+    const float2 t = cs_tab[lane];
+    const float x0 = bf16_bits_to_f32(kw & 0xffffu), x1 = bf16_bits_to_f32(kw >> 16);
+    knew = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+    if (wave == 0) {
+      reinterpret_cast<uint32_t*>(a.k_cache)[(cslot >> 1) + lane] = knew;
+      reinterpret_cast<uint32_t*>(a.v_cache)[(cslot >> 1) + lane] = vnew;
+    }
+  }
+
+  // Q^T B operand: column n = head kvh*G + n rotated at L (zeros for n >= G);
+  // k-step s holds dims 32s + 8g .. +7, i.e. pairs 16s + 4g .. +3.
   bf16x8_t qf[HD / 32];
   {
-    const uint4* src = reinterpret_cast<const uint4*>(a.q_rot + ((long)b * a.H + head) * HD);
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                      ((long)b * a.H + head) * HD);
 #pragma unroll
-    for (int s = 0; s < HD / 32; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8_t, qcol ? src[4 * s + g] : make_uint4(0, 0, 0, 0));
+    for (int s = 0; s < HD / 32; ++s) {
+      const uint4 wv = qcol ? src[4 * s + g] : make_uint4(0, 0, 0, 0);
+      const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+      uint32_t d[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float2 t = cs_tab[16 * s + 4 * g + p];
+        const float x0 = bf16_bits_to_f32(w4[p] & 0xffffu), x1 = bf16_bits_to_f32(w4[p] >> 16);
+        d[p] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+    }
   }
   const float c2 = a.scale_log2;
   const float slope2 = a.alibi ? alibi_slope(a.alibi, head, a.H) * kLog2e : 0.f;
@@ -220,33 +256,42 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   for (int db = 0; db < HD / 16; ++db) oacc[db] = f32x4_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  uint4 kr[LOADS], vr[LOADS];
-  auto load_tile = [&](int ts) {
+  // Two tiles of K/V in flight per wave: slot t&1 holds tile t until it is
+  // written to LDS, then receives tile t+2. Buffer descriptors start at the tile
+  // and end at key slot nk, so rows past the sequence end read as zero.
+  uint4 kr[2][LOADS], vr[2][LOADS];
+  auto load_tile = [&](int slot, int ts) {
+    const int bytes = (nk - ts) * HD * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)ts * HD, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)ts * HD, bytes);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int e = lane + 64 * i;
-      const int r = e / KCH, c = e % KCH;
-      const bool in = ts + r < nk;
-      const long off = (long)(ts + r) * HD + c * 8;
-      kr[i] = in ? *reinterpret_cast<const uint4*>(Kg + off) : make_uint4(0, 0, 0, 0);
-      vr[i] = in ? *reinterpret_cast<const uint4*>(Vg + off) : make_uint4(0, 0, 0, 0);
+      kr[slot][i] = buffer_load16(rk, 16 * (lane + 64 * i));
+      vr[slot][i] = buffer_load16(rv, 16 * (lane + 64 * i));
     }
   };
-  load_tile(k0 + wave * kTile);
+  const auto tile_start = [&](int t) { return k0 + (t * kWaves + wave) * kTile; };
+  if (tile_start(0) < nk) load_tile(0, tile_start(0));
+  if (kTilesPerWave > 1 && tile_start(1) < nk) load_tile(1, tile_start(1));
 
-#pragma unroll 1
+#pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
-    const int ts = k0 + (t * kWaves + wave) * kTile;
+    const int ts = tile_start(t);
     if (ts >= nk) break;
+    const int slot = t & 1;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int e = lane + 64 * i;
       const int r = e / KCH, c = e % KCH;
-      *reinterpret_cast<uint4*>(kl + dk_off<HD>(r, c)) = kr[i];
-      *reinterpret_cast<uint4*>(vl + dv_off<HD>(r, c)) = vr[i];
+      *reinterpret_cast<uint4*>(kl + dk_off<HD>(r, c)) = kr[slot][i];
+      *reinterpret_cast<uint4*>(vl + dv_off<HD>(r, c)) = vr[slot][i];
     }
-    const int tn = ts + kWaves * kTile;
-    if (t + 1 < kTilesPerWave && tn < nk) load_tile(tn);
+    if (own_slot && L >= ts && L < ts + kTile && lane < HD / 2) {
+      const int r = L - ts;  // pair `lane` sits in chunk lane/4, bytes 4*(lane%4)
+      *reinterpret_cast<uint32_t*>(kl + dk_off<HD>(r, lane >> 2) + 4 * (lane & 3)) = knew;
+      *reinterpret_cast<uint32_t*>(vl + dv_off<HD>(r, lane >> 2) + 4 * (lane & 3)) = vnew;
+    }
+    if (t + 2 < kTilesPerWave && tile_start(t + 2) < nk) load_tile(slot, tile_start(t + 2));
 
     // S^T = K Q^T for the tile's two 16-key blocks
     f32x4_t sacc[2];
@@ -423,14 +468,15 @@ hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHoo
   const bool mfma = decode_mfma_supported(a, BF16);
   a.split = mfma ? kSplitMfma : kDecodeSplit;
   a.nsplit = (a.Lmax + a.split - 1) / a.split;
-  if (!mfma) a.q_rot = nullptr;
-  hipLaunchKernelGGL(decode_append_kernel<BF16>, dim3(a.KV, a.B), dim3(HD / 2), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!mfma) {  // the MFMA split kernel appends the new token itself
+    hipLaunchKernelGGL(decode_append_kernel<BF16>, dim3(a.KV, a.B), dim3(HD / 2), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if ((e = tm.before(s)) != hipSuccess) return e;
   if (mfma) {
     if constexpr (HD == 64 || HD == 128) {
-      hipLaunchKernelGGL((decode_split_mfma_kernel<HD>), dim3(a.nsplit, a.KV, a.B), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_split_mfma_kernel<HD>), dim3(a.KV * a.B, a.nsplit), dim3(256), 0, s, a);
     }
   } else {
     hipLaunchKernelGGL((decode_split_valu_kernel<BF16, HD>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, s, a);

@@ -257,6 +257,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int w = blockIdx.x;
   int unit, qrank;
   if (gm.xcd_aware) {
+    // Consecutive workgroups go round-robin to the 8 XCDs. XCD x owns units
+    // [x*upx, (x+1)*upx) and interleaves them, heaviest query blocks first.
+    // (Working through one unit at a time measured slower: all of an XCD's
+    // workgroups then hit the same K/V lines at once.)
     const int upx = gm.units >> 3;
     const int j = w >> 3;
     unit = (w & 7) * upx + j % upx;
