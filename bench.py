@@ -213,8 +213,8 @@ def main():
     ap.add_argument("--workload", default="all", choices=["all", "prefill", "decode", "alibi", "small", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
-    ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--cpu-seqs", type=int, default=64)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
