@@ -127,6 +127,12 @@ __device__ __forceinline__ void rope_cos_sin(int pos, double q4, float& c, float
   c = ((q + 1) & 2) ? -c1 : c1;
 }
 
+// Rotate the pair (x0, x1) by the angle with cosine c and sine s. Written with
+// explicit FMAs so every kernel rounds the rotation identically (the compiler
+// may not contract these differently in different call sites).
+__device__ __forceinline__ float rot0(float x0, float x1, float c, float s) { return fmaf(x0, c, -(x1 * s)); }
+__device__ __forceinline__ float rot1(float x0, float x1, float c, float s) { return fmaf(x0, s, x1 * c); }
+
 // ALiBi slope of head h out of H for the two slope families, in fp32.
 __device__ __forceinline__ float alibi_slope(int kind, int h, int H) {
   const float e = (kind == 1 ? -8.0f : -2.0f) * (float)(h + 1) / (float)H;

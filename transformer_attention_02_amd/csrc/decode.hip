@@ -42,7 +42,7 @@ __global__ void decode_append_kernel(DecodeArgs a) {
   const long src = ((long)b * a.KV + g) * a.hd + 2 * p;
   const long dst = (((long)b * a.KV + g) * a.Lmax + L) * a.hd + 2 * p;
   const float x0 = ld<BF16>(a.k_new, src), x1 = ld<BF16>(a.k_new, src + 1);
-  const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
+  const float y0 = rot0(x0, x1, c, s), y1 = rot1(x0, x1, c, s);
   if constexpr (BF16) {
     reinterpret_cast<uint32_t*>(a.k_cache)[dst >> 1] = pack_bf16x2(y0, y1);
     reinterpret_cast<uint32_t*>(a.v_cache)[dst >> 1] = reinterpret_cast<const uint32_t*>(a.v_new)[src >> 1];
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_split_valu_kernel(DecodeArgs a) {
     if (a.rope) {
       float c, s;
       rope_cos_sin(L, a.freqs.rev[t], c, s);
-      const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
+      const float y0 = rot0(x0, x1, c, s), y1 = rot1(x0, x1, c, s);
       x0 = y0;
       x1 = y1;
     }
@@ -215,7 +215,7 @@ void decode_split_mfma_kernel(DecodeArgs a) {
     vnew = reinterpret_cast<const uint32_t*>(a.v_new)[(nslot >> 1) + lane];
     const float2 t = cs_tab[lane];
     const float x0 = bf16_bits_to_f32(kw & 0xffffu), x1 = bf16_bits_to_f32(kw >> 16);
-    knew = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+    knew = pack_bf16x2(rot0(x0, x1, t.x, t.y), rot1(x0, x1, t.x, t.y));
     if (wave == 0) {
       reinterpret_cast<uint32_t*>(a.k_cache)[(cslot >> 1) + lane] = knew;
       reinterpret_cast<uint32_t*>(a.v_cache)[(cslot >> 1) + lane] = vnew;
@@ -237,7 +237,7 @@ void decode_split_mfma_kernel(DecodeArgs a) {
       for (int p = 0; p < 4; ++p) {
         const float2 t = cs_tab[16 * s + 4 * g + p];
         const float x0 = bf16_bits_to_f32(w4[p] & 0xffffu), x1 = bf16_bits_to_f32(w4[p] >> 16);
-        d[p] = pack_bf16x2(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+        d[p] = pack_bf16x2(rot0(x0, x1, t.x, t.y), rot1(x0, x1, t.x, t.y));
       }
       qf[s] = __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
     }

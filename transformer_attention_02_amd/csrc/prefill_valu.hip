@@ -58,14 +58,14 @@ __global__ __launch_bounds__(256) void rope_k_kernel(RopeKArgs a) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float x0 = bf16_bits_to_f32(w[p] & 0xffffu), x1 = bf16_bits_to_f32(w[p] >> 16);
-        w[p] = pack_bf16x2(x0 * cs[p] - x1 * sn[p], x0 * sn[p] + x1 * cs[p]);
+        w[p] = pack_bf16x2(rot0(x0, x1, cs[p], sn[p]), rot1(x0, x1, cs[p], sn[p]));
       }
       y = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
       const float f0 = __uint_as_float(x[j].x), f1 = __uint_as_float(x[j].y);
       const float f2 = __uint_as_float(x[j].z), f3 = __uint_as_float(x[j].w);
-      y = make_uint4(__float_as_uint(f0 * cs[0] - f1 * sn[0]), __float_as_uint(f0 * sn[0] + f1 * cs[0]),
-                     __float_as_uint(f2 * cs[1] - f3 * sn[1]), __float_as_uint(f2 * sn[1] + f3 * cs[1]));
+      y = make_uint4(__float_as_uint(rot0(f0, f1, cs[0], sn[0])), __float_as_uint(rot1(f0, f1, cs[0], sn[0])),
+                     __float_as_uint(rot0(f2, f3, cs[1], sn[1])), __float_as_uint(rot1(f2, f3, cs[1], sn[1])));
     }
     dst[e] = y;
   }
@@ -95,8 +95,8 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
     if (a.rope) {
       float c, s;
       rope_cos_sin(a.pos0 + i, a.freqs.rev[p], c, s);
-      y0 = x0 * c - x1 * s;
-      y1 = x0 * s + x1 * c;
+      y0 = rot0(x0, x1, c, s);
+      y1 = rot1(x0, x1, c, s);
     }
     q[2 * p] = y0 * a.scale_log2;
     q[2 * p + 1] = y1 * a.scale_log2;
