@@ -44,24 +44,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;  // keys per tile
 constexpr int NW = 4;   // waves per workgroup
+constexpr int kKAhead = 8;  // K operand reads in flight ahead of the score MFMAs
 constexpr int NT = NW * 64;
 
 template <int HD>
 struct Cfg {
   static constexpr int KCH = HD / 8;               // 16-byte chunks per key row
-  // Padded row pitches keep every MFMA operand read free of LDS bank conflicts
-  // while leaving the addresses affine (a per-lane base plus immediates):
-  //  * K rows (pitch 2hd + 16): the 16 lanes of a ds_read_b128 read one 16-byte
-  //    chunk of 16 different rows, which land on 16 disjoint 4-bank groups;
-  //  * V rows (pitch 2hd + 64): a transposing load reads 4 consecutive rows x
-  //    32 bytes per 16-lane group (64 bytes for the 32 lanes served together),
-  //    and the 64-byte skew puts the 4 rows on disjoint bank ranges.
-  static constexpr int KP = HD * 2 + 16;
-  static constexpr int VP = HD * 2 + 64;
-  static constexpr int K_BYTES = BN * KP;          // K tile, row-major [key][hd]
-  static constexpr int V_BYTES = BN * VP;          // V tile, row-major [key][hd]
+  static constexpr int K_BYTES = BN * HD * 2;      // K tile, row-major [key][hd], XOR-swizzled chunks
+  static constexpr int V_BYTES = BN * HD * 2;      // V tile, row-major [key][hd], XOR-swizzled chunks
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int LOADS = BN * KCH / NT;      // 16-byte loads per thread per tensor
+  static constexpr int DMA = K_BYTES / 1024;       // 1 KiB LDS-DMA wave instructions per tensor per tile
 };
 
 struct GridMap {
@@ -73,11 +65,40 @@ struct GridMap {
   int xcd_aware;
 };
 
-// Byte offset of 16-byte chunk `c` of key row `r` in the K / V tile.
+// XOR swizzles of the 16-byte chunk index. Rows are unpadded (so one LDS-DMA
+// wave instruction fills 1 KiB of whole rows) and the swizzles keep every MFMA
+// operand read free of bank conflicts (measured: SQ_LDS_BANK_CONFLICT = 0):
+//  * K: the 16 lanes of a ds_read_b128 read one logical chunk of 16 different
+//    rows; XOR with the row's low bits sends them to 16 different chunk slots;
+//  * V: a transposing load reads rows r..r+3 x 32 bytes per 16-lane group (64
+//    bytes per 32 lanes); XOR with (r & 3) << 2 moves each row to its own
+//    64-byte bank range.
 template <int HD>
-__device__ __forceinline__ int k_off(int r, int c) { return r * Cfg<HD>::KP + c * 16; }
+__host__ __device__ constexpr int k_swz(int r) {
+  return HD == 128 ? (r & 15) : ((r >> 1) & 7);
+}
 template <int HD>
-__device__ __forceinline__ int v_off(int r, int c) { return r * Cfg<HD>::VP + c * 16; }
+__host__ __device__ constexpr int v_swz(int r) {
+  return HD == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+// Byte offset of logical 16-byte chunk `c` of key row `r` in the K / V tile.
+template <int HD>
+__host__ __device__ constexpr int k_off(int r, int c) { return r * HD * 2 + ((c ^ k_swz<HD>(r)) << 4); }
+template <int HD>
+__host__ __device__ constexpr int v_off(int r, int c) { return r * HD * 2 + ((c ^ v_swz<HD>(r)) << 4); }
+
+// The V swizzle depends on the row only through bits that a step of 4 rows
+// keeps, so each lane's transposing-load addresses for the rows r + 4e + 16u
+// are its row-r address plus a constant (an instruction offset).
+template <int HD>
+constexpr bool v_rows_affine() {
+  for (int r0 = 0; r0 < 12; ++r0)
+    for (int d = 0; d < 64 - 12; d += 4)
+      for (int c = 0; c < HD / 8; ++c)
+        if (v_off<HD>(r0 + d, c) != v_off<HD>(r0, c) + d * HD * 2) return false;
+  return true;
+}
+static_assert(v_rows_affine<64>() && v_rows_affine<128>(), "V swizzle must be invariant under 4-row steps");
 
 // Swap bits 2 and 3 of a row index in [0, 32).
 __device__ __forceinline__ int perm_row(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -91,38 +112,44 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
 
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
 
-// Registers holding one K/V tile between its global load and its LDS store.
-// Thread t moves chunks e = t + 256 i (key row e / KCH, 16-byte chunk e % KCH)
-// of both tensors; every wave instruction covers whole rows, so the global
-// loads are fully coalesced and the LDS stores are conflict-free.
-template <int HD>
-struct Stage {
-  using C = Cfg<HD>;
-  uint4 k[C::LOADS];
-  uint4 v[C::LOADS];
+#define LDS __attribute__((address_space(3)))
+typedef const LDS unsigned char* LdsBytes;  // operand reads address LDS directly
 
-  // Loads tile kt through buffer descriptors that start at the tile and end at
-  // the slab end: rows at or past T read as zero.
-  __device__ __forceinline__ void load(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, int tid) {
+// Direct global -> LDS staging of one K/V tile (no registers in between). Wave
+// w issues wave instructions q = w*DMA/4 .. of 1 KiB each per tensor; lane l of
+// instruction q fills LDS bytes 1024q + 16l, i.e. key row r = (1024q + 16l) /
+// (2hd) at physical chunk pc, so it fetches the logical chunk pc ^ swz(r) of
+// that row. The buffer descriptor starts at the tile and ends at the slab end:
+// rows at or past T are written as zeros.
+template <int HD>
+struct Dma {
+  using C = Cfg<HD>;
+  static constexpr int PER_WAVE = C::DMA / NW;
+  int koff[PER_WAVE];  // per-lane source byte offsets within the tile
+  int voff[PER_WAVE];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int p = 1024 * (wave * PER_WAVE + i) + 16 * lane;
+      const int r = p / (HD * 2), pc = (p % (HD * 2)) / 16;
+      koff[i] = (r * HD + (pc ^ k_swz<HD>(r)) * 8) * 2;
+      voff[i] = (r * HD + (pc ^ v_swz<HD>(r)) * 8) * 2;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, unsigned char* stage,
+                                        int wave) const {
     const int bytes = (T - kt * BN) * HD * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)kt * BN * HD, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)kt * BN * HD, bytes);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int e = tid + NT * i;  // row e / KCH, chunk e % KCH: byte offset 16 e
-      k[i] = buffer_load16(rk, 16 * e);
-      v[i] = buffer_load16(rv, 16 * e);
-    }
-  }
-
-  __device__ __forceinline__ void store(unsigned char* kb, int tid) const {
-    unsigned char* vb = kb + C::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int e = tid + NT * i;
-      const int r = e / C::KCH, c = e % C::KCH;
-      *reinterpret_cast<uint4*>(kb + k_off<HD>(r, c)) = k[i];
-      *reinterpret_cast<uint4*>(vb + v_off<HD>(r, c)) = v[i];
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave * PER_WAVE + i;
+#if defined(__HIP_DEVICE_COMPILE__)  // (the host pass drops the kernel stubs of later instantiations otherwise)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(stage + 1024 * q), 16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(stage + C::K_BYTES + 1024 * q), 16, voff[i], 0, 0, 0);
+#endif
     }
   }
 };
@@ -143,11 +170,29 @@ struct WaveState {
   int qi;                    // this lane's query row in block 0
   int T;
   int lane;
+  int vtr[HD / 32];          // byte offset (from the K tile start) of this lane's V^T read, key row 8hf + (lane%16)/4
+
+  // The offsets are made opaque to the optimizer: otherwise it re-derives
+  // each address from a neighbouring one in long pointer chains, and the
+  // compiler then can no longer tell which LDS stage a read touches and waits
+  // for the DMA into the other stage before it.
+  __device__ __forceinline__ void init_offsets() {
+    using C = Cfg<HD>;
+    const int li = lane & 15, hf = lane >> 5;
+#pragma unroll
+    for (int mb = 0; mb < HD / 32; ++mb) {
+      const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+      int o = C::K_BYTES + v_off<HD>(8 * hf + (li >> 2), col >> 3) + (col & 7) * 2;
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("" : "+v"(o));
+#endif
+      vtr[mb] = o;
+    }
+  }
 
   template <bool MASK>
-  __device__ __forceinline__ void tile(const unsigned char* kb, int k0) {
+  __device__ __forceinline__ void tile(LdsBytes kb, int k0) {
     using C = Cfg<HD>;
-    const unsigned char* vb = kb + C::K_BYTES;
     const int n = lane & 31, hf = lane >> 5;
     // S^T = K Q^T; the K rows are read in permuted order (perm_row) so that
     // register i of the two accumulators holds key k0 + 32(i/16) + 16((i%16)/8) + 8hf + i%8.
@@ -159,11 +204,24 @@ struct WaveState {
       for (int j = 0; j < QB; ++j) sacc[j][kb2] = f32x16{};
 #pragma unroll
       for (int s = 0; s < HD / 16; ++s) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(kb + k_off<HD>(32 * kb2 + krow, 2 * s + hf)));
+        const bf16x8 av = *reinterpret_cast<const LDS bf16x8*>(kb + k_off<HD>(32 * kb2 + krow, 2 * s + hf));
 #pragma unroll
         for (int j = 0; j < QB; ++j)
           sacc[j][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[j][s], sacc[j][kb2], 0, 0, 0);
       }
+    }
+    // Issue order of the score products: the first kKAhead operand reads go
+    // out before any MFMA, then one read per MFMA, so LDS latency hides behind
+    // kKAhead MFMAs instead of one.
+    {
+      constexpr int NR = 2 * (HD / 16), NM = NR * QB;
+      __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
+#pragma unroll
+      for (int i = 0; i < NR - kKAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - QB * (NR - kKAhead), 0);
     }
     bf16x8 pb[QB][4];
     bool live[QB];
@@ -234,17 +292,13 @@ struct WaveState {
     // from the probabilities; V^T is read with transposing loads: source lane i
     // of a 16-lane group points at key row 16u + 8hf + i/4 (+4), columns
     // d0 + 4(i%4), and lane i then holds V[those 4 keys][d0 + i].
-    const int li = lane & 15;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int mb = 0; mb < HD / 32; ++mb) {
-        const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-        const int r = 16 * u + 8 * hf + (li >> 2);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r, col >> 3) + (col & 7) * 2));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + v_off<HD>(r + 4, col >> 3) + (col & 7) * 2));
+        LdsBytes p = kb + vtr[mb] + 16 * u * HD * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p + 4 * HD * 2));
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int j = 0; j < QB; ++j)
@@ -254,12 +308,10 @@ struct WaveState {
   }
 };
 
-// QB = query blocks of 32 rows per wave. QB = 2: one wave per SIMD (the state
-// needs ~400 VGPRs) and a 3-stage LDS ring, so tile t+2 is in flight while tile
-// t is computed. QB = 1: two waves per SIMD and a double buffer.
+// QB = query blocks of 32 rows per wave: QB = 1 runs two waves per SIMD, QB = 2
+// one (its state needs ~400 VGPRs).
 template <int QB>
 struct Sched {
-  static constexpr int STAGES = QB == 2 ? 3 : 2;
   static constexpr int WAVES_PER_EU = QB == 2 ? 1 : 2;
 };
 
@@ -267,8 +319,11 @@ template <int HD, bool ALIBI, bool CAUSAL, bool OUT_BF16, int QB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Sched<QB>::WAVES_PER_EU, Sched<QB>::WAVES_PER_EU)))
 void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using C = Cfg<HD>;
-  constexpr int STAGES = Sched<QB>::STAGES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * C::STAGE];
+  // Two stage buffers as separate LDS objects: the compiler then knows that the
+  // DMA filling one stage cannot alias the reads of the other, and does not
+  // wait for the in-flight tile before reading the current one.
+  __shared__ __attribute__((aligned(16))) unsigned char s0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char s1[C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -309,14 +364,16 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   const int q_last = min(a.T, q0 + gm.bm) - 1;
   const int nkt = CAUSAL ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
 
-  // The first K/V tile's global loads are in flight during the Q set-up.
-  Stage<HD> st;
-  st.load(Kg, Vg, 0, a.T, tid);
+  // The first K/V tile streams into stage 0 during the Q set-up.
+  Dma<HD> dma;
+  dma.init(wave, lane);
+  dma.issue(Kg, Vg, 0, a.T, s0, wave);
 
   WaveState<HD, ALIBI, CAUSAL, QB> ws;
   ws.qi = qw0 + n;
   ws.T = a.T;
   ws.lane = lane;
+  ws.init_offsets();
   ws.c2 = a.scale_log2;
   ws.slope2 = ALIBI ? alibi_slope(a.alibi, head, a.H) * 1.4426950408889634f : 0.f;
 #pragma unroll
@@ -328,12 +385,12 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   }
 
   // ---- Q rows -> B operands (rotated in fp32, rounded to bf16). When it fits
-  // in LDS, the rotary cos/sin of the workgroup's bm rows are computed once
-  // (layout [pair][row], so lanes reading consecutive rows hit distinct banks)
-  // and shared by the waves of all heads in the workgroup.
+  // in the stage-1 area, the rotary cos/sin of the workgroup's bm rows are
+  // computed once (layout [pair][row], so lanes reading consecutive rows hit
+  // distinct banks) and shared by the waves of all heads in the workgroup.
   {
-    const bool table = a.rope && (HD / 2) * gm.bm * (int)sizeof(float2) <= STAGES * C::STAGE;
-    float2* cs = reinterpret_cast<float2*>(smem);  // [HD/2][bm]
+    const bool table = a.rope && (HD / 2) * gm.bm * (int)sizeof(float2) <= C::STAGE;
+    float2* cs = reinterpret_cast<float2*>(s1);  // [HD/2][bm]
     if (table) {
       for (int e = tid; e < (HD / 2) * gm.bm; e += NT) {
         const int r = e % gm.bm, p = e / gm.bm;
@@ -381,39 +438,49 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
         for (int s = 0; s < HD / 16; ++s) ws.qf[j][s] = rotate(raw[s], qr, 8 * s + 4 * hf);
       }
     }
-    if (table) __syncthreads();  // the table area is reused by the K/V tiles
   }
-
-  st.store(smem, tid);
-  if constexpr (STAGES == 3) {
-    if (nkt > 1) st.load(Kg, Vg, 1, a.T, tid);
-  }
+  // Tile 0 has landed and no wave still reads the table area (stage 1).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // Tiles [0, kt_clean) need no mask for any row of the workgroup: every key is
   // at or before the first query row (causal) and inside the sequence.
   const int kt_clean = min(nkt, CAUSAL ? min((q0 + 1) / BN, a.T / BN) : a.T / BN);
-  auto step = [&](int kt, auto mask_tag) {
+  // Double buffer: tile kt+1 streams into the other stage while tile kt is
+  // computed; the wait + barrier at the end publishes it and retires stage kt.
+  // The stage parity is a compile-time constant of each step.
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  auto step = [&](int kt, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int P = decltype(par_tag)::value;
+    unsigned char* cur = P ? s1 : s0;
+    unsigned char* nxt = P ? s0 : s1;
     const int k0 = kt * BN;
-    if constexpr (STAGES == 3) {
-      // registers hold tile kt+1 (loaded one step ago): store it, then fetch kt+2
-      if (kt + 1 < nkt) st.store(smem + ((kt + 1) % 3) * C::STAGE, tid);
-      if (kt + 2 < nkt) st.load(Kg, Vg, kt + 2, a.T, tid);
-    } else {
-      if (kt + 1 < nkt) st.load(Kg, Vg, kt + 1, a.T, tid);
-    }
-    const unsigned char* kb = smem + (kt % STAGES) * C::STAGE;
+    if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.T, nxt, wave);
     const bool run = wave_active && !(MASK && CAUSAL && k0 > qw0 + 32 * QB - 1);
-    if (run) ws.template tile<MASK>(kb, k0);
-    if constexpr (STAGES == 2) {
-      if (kt + 1 < nkt) st.store(smem + ((kt + 1) & 1) * C::STAGE, tid);
-    }
+    if (run) ws.template tile<MASK>((LdsBytes)cur, k0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   int kt = 0;
-  for (; kt < kt_clean; ++kt) step(kt, std::integral_constant<bool, false>{});
-  for (; kt < nkt; ++kt) step(kt, std::integral_constant<bool, true>{});
+  auto phase = [&](int end, auto mask_tag) __attribute__((always_inline)) {
+    if (kt & 1) {
+      while (kt < end) {
+        step(kt++, mask_tag, Odd{});
+        if (kt >= end) break;
+        step(kt++, mask_tag, Even{});
+      }
+    } else {
+      while (kt < end) {
+        step(kt++, mask_tag, Even{});
+        if (kt >= end) break;
+        step(kt++, mask_tag, Odd{});
+      }
+    }
+  };
+  phase(kt_clean, std::integral_constant<bool, false>{});
+  phase(nkt, std::integral_constant<bool, true>{});
 
   if (!wave_active) return;
 #pragma unroll
