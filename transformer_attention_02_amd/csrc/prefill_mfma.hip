@@ -6,9 +6,9 @@
 // softmax statistics and accumulation (that page's mixed-precision roadmap item).
 //
 // Work decomposition
-//   * A workgroup is 4 waves. It owns one block of query rows for up to 4 query
-//     heads that share one key/value head (grouped-query packing), so every
-//     K/V tile staged in LDS serves all of them.
+//   * A workgroup is 8 waves (two per SIMD). It owns one block of query rows
+//     for up to 4 query heads that share one key/value head (grouped-query
+//     packing), so every K/V tile staged in LDS serves 256 query rows.
 //   * A wave owns 32 query rows of one head and computes S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16. In the 32x32 accumulator a lane holds one
 //     query (column) and 16 keys (rows), so the row max and row sum are
@@ -17,11 +17,14 @@
 //     the row index swapped) so that accumulator registers 8u..8u+7 of a lane
 //     hold 8 consecutive keys: the probabilities then feed O^T = V^T P^T as the
 //     B operand straight from registers (rounded to bf16).
-//   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
-//     j+1 are in flight while tile j is computed. Both tiles are stored
-//     row-major as loaded; V^T operands are read with ds_read_b64_tr_b16 (the
-//     transposing LDS load of gfx950). Padded row pitches keep the operand
-//     reads free of bank conflicts.
+//   * The V^T P^T product of tile j is deferred to tile j+1 and issued between
+//     the instructions of tile j+1's softmax: the matrix core and the vector
+//     ALU of one wave then work at the same time.
+//   * K/V tiles of 64 keys go global -> LDS by DMA (buffer loads that write LDS
+//     directly) into a 3-stage ring: tile j+1 lands while tile j is computed
+//     and V of tile j-1 is still read. Tiles are stored row-major with XOR-
+//     swizzled 16-byte chunks; V^T operands are read with ds_read_b64_tr_b16
+//     (the transposing LDS load of gfx950).
 //   * Causal: tiles past the diagonal are never loaded; a wave skips tiles that
 //     are entirely above its rows; only tiles crossing the diagonal (or the
 //     ragged end of the sequence) are masked.
@@ -41,10 +44,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;  // keys per tile
-constexpr int NW = 4;   // waves per workgroup
-constexpr int kKAhead = 8;  // K operand reads in flight ahead of the score MFMAs
+constexpr int NW = 8;   // waves per workgroup (two per SIMD)
+constexpr int kKAhead = 4;       // K operand reads issued ahead of the score MFMAs
+constexpr int kValuPerMfma = 8;  // softmax instructions issued per deferred V^T MFMA
 constexpr int NT = NW * 64;
 
 template <int HD>
@@ -59,7 +64,7 @@ struct Cfg {
 struct GridMap {
   int hpw;       // heads per workgroup (1, 2 or 4)
   int hchunks;   // group / hpw
-  int bm;        // query rows per head per workgroup = 32 * QB * (4 / hpw)
+  int bm;        // query rows per head per workgroup = 32 * (NW / hpw)
   int nqb;       // query blocks
   int units;     // B * KV * hchunks
   int xcd_aware;
@@ -116,7 +121,7 @@ __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
 typedef const LDS unsigned char* LdsBytes;  // operand reads address LDS directly
 
 // Direct global -> LDS staging of one K/V tile (no registers in between). Wave
-// w issues wave instructions q = w*DMA/4 .. of 1 KiB each per tensor; lane l of
+// w issues wave instructions q = w*DMA/NW .. of 1 KiB each per tensor; lane l of
 // instruction q fills LDS bytes 1024q + 16l, i.e. key row r = (1024q + 16l) /
 // (2hd) at physical chunk pc, so it fetches the logical chunk pc ^ swz(r) of
 // that row. The buffer descriptor starts at the tile and ends at the slab end:
@@ -125,6 +130,7 @@ template <int HD>
 struct Dma {
   using C = Cfg<HD>;
   static constexpr int PER_WAVE = C::DMA / NW;
+  static_assert(C::DMA % NW == 0, "every wave issues the same share of a tile");
   int koff[PER_WAVE];  // per-lane source byte offsets within the tile
   int voff[PER_WAVE];
 
@@ -154,35 +160,32 @@ struct Dma {
   }
 };
 
-// One wave's online-softmax state over QB blocks of 32 query rows (rows qi + 32j
-// for block j), and the work of one 64-key tile. Each K and V operand read from
-// LDS feeds the MFMAs of all QB blocks. MASK selects the variant for tiles that
-// cross the causal diagonal or the sequence end; every other tile runs without
-// masking code.
-template <int HD, bool ALIBI, bool CAUSAL, int QB>
+// One wave's online-softmax state for 32 query rows (lane n holds row qi, the
+// two half-waves split the keys of a tile), and the steps of one 64-key tile.
+template <int HD, bool ALIBI, bool CAUSAL>
 struct WaveState {
-  f32x16 oacc[QB][HD / 32];  // O^T: lane holds query n, dims 32mb + 8(r/4) + 4hf + r%4
-  bf16x8 qf[QB][HD / 16];    // Q^T B operand, k-step s: dims 16s + 8hf .. +7
-  float m_run[QB];           // running max (log2 units), per row
-  float l_run[QB];           // this half-wave's part of the running denominator
-  float c2;                  // log2(e) / sqrt(hd)
-  float slope2;              // ALiBi slope * log2(e)
-  int qi;                    // this lane's query row in block 0
+  f32x16 oacc[HD / 32];  // O^T: lane holds query n, dims 32mb + 8(r/4) + 4hf + r%4
+  bf16x8 qf[HD / 16];    // Q^T B operand, k-step s: dims 16s + 8hf .. +7
+  bf16x8 pprev[4];       // P^T operands (keys 16u + 8hf .. +7) whose V^T product is still due
+  float m_run;           // running max (log2 units)
+  float l_run;           // this half-wave's part of the running denominator
+  float c2;              // log2(e) / sqrt(hd)
+  float slope2;          // ALiBi slope * log2(e)
+  int qi;                // this lane's query row
   int T;
   int lane;
-  int vtr[HD / 32];          // byte offset (from the K tile start) of this lane's V^T read, key row 8hf + (lane%16)/4
+  int vtr[HD / 32];      // byte offset in the V tile of this lane's V^T read, key row 8hf + (lane%16)/4
 
   // The offsets are made opaque to the optimizer: otherwise it re-derives
   // each address from a neighbouring one in long pointer chains, and the
   // compiler then can no longer tell which LDS stage a read touches and waits
-  // for the DMA into the other stage before it.
+  // for the DMA into another stage before it.
   __device__ __forceinline__ void init_offsets() {
-    using C = Cfg<HD>;
     const int li = lane & 15, hf = lane >> 5;
 #pragma unroll
     for (int mb = 0; mb < HD / 32; ++mb) {
       const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-      int o = C::K_BYTES + v_off<HD>(8 * hf + (li >> 2), col >> 3) + (col & 7) * 2;
+      int o = v_off<HD>(8 * hf + (li >> 2), col >> 3) + (col & 7) * 2;
 #if defined(__HIP_DEVICE_COMPILE__)
       asm volatile("" : "+v"(o));
 #endif
@@ -190,140 +193,153 @@ struct WaveState {
     }
   }
 
-  template <bool MASK>
-  __device__ __forceinline__ void tile(LdsBytes kb, int k0) {
-    using C = Cfg<HD>;
+  // S^T = K Q^T for the 64 keys of the K tile at kb. The K rows are read in
+  // permuted order (perm_row) so that register i of s[i/16] holds key
+  // k0 + 32(i/16) + 16((i%16)/8) + 8hf + i%8.
+  __device__ __forceinline__ void scores(LdsBytes kb, f32x16& sa, f32x16& sb) const {
     const int n = lane & 31, hf = lane >> 5;
-    // S^T = K Q^T; the K rows are read in permuted order (perm_row) so that
-    // register i of the two accumulators holds key k0 + 32(i/16) + 16((i%16)/8) + 8hf + i%8.
-    f32x16 sacc[QB][2];
     const int krow = perm_row(n);
+    sa = f32x16{};
+    sb = f32x16{};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int j = 0; j < QB; ++j) sacc[j][kb2] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < HD / 16; ++s) {
-        const bf16x8 av = *reinterpret_cast<const LDS bf16x8*>(kb + k_off<HD>(32 * kb2 + krow, 2 * s + hf));
-#pragma unroll
-        for (int j = 0; j < QB; ++j)
-          sacc[j][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[j][s], sacc[j][kb2], 0, 0, 0);
-      }
+    for (int s = 0; s < HD / 16; ++s) {
+      const bf16x8 av = *reinterpret_cast<const LDS bf16x8*>(kb + k_off<HD>(krow, 2 * s + hf));
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[s], sa, 0, 0, 0);
     }
-    // Issue order of the score products: the first kKAhead operand reads go
-    // out before any MFMA, then one read per MFMA, so LDS latency hides behind
-    // kKAhead MFMAs instead of one.
-    {
-      constexpr int NR = 2 * (HD / 16), NM = NR * QB;
-      __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
 #pragma unroll
-      for (int i = 0; i < NR - kKAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - QB * (NR - kKAhead), 0);
+    for (int s = 0; s < HD / 16; ++s) {
+      const bf16x8 av = *reinterpret_cast<const LDS bf16x8*>(kb + k_off<HD>(32 + krow, 2 * s + hf));
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[s], sb, 0, 0, 0);
     }
-    bf16x8 pb[QB][4];
-    bool live[QB];
+    // Issue order: kKAhead operand reads go out before the first MFMA, then
+    // one read per MFMA, so LDS latency hides behind kKAhead MFMAs.
+    constexpr int NR = 2 * (HD / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
 #pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      const int qj = qi + 32 * j;
-      // a block whose rows all precede the tile's first key contributes nothing
-      live[j] = !(MASK && CAUSAL && k0 > (qi - n) + 32 * j + 31);
-      if (!live[j]) continue;
-      // Without ALiBi t keeps the raw scores (the max commutes with the positive
-      // scale, which is folded into the exponent's FMA); with ALiBi t is the
-      // scaled, biased score in log2 units.
-      float t[32];
-      const int dbase = k0 + 8 * hf - qj;  // key - query at register offset 0
-      if constexpr (ALIBI) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float dk = (float)(dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8));
-          t[i] = fmaf(sacc[j][i / 16][i % 16], c2, slope2 * (CAUSAL ? dk : -fabsf(dk)));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) t[i] = sacc[j][i / 16][i % 16];
-      }
-      if constexpr (MASK) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int dk = dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
-          const bool vis = (dk + qj < T) && (!CAUSAL || dk <= 0);
-          t[i] = vis ? t[i] : -INFINITY;
-        }
-      }
-      float mx = t[0];
-#pragma unroll
-      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, t[i]);
-      mx = fmaxf(mx, xhalf(mx));
-      const float ms = ALIBI ? mx : mx * c2;  // tile max in log2 units
-      // Lazy rescale: a row's running max only moves when its tile max exceeds
-      // it by more than 8 (a factor 2^8); otherwise the stale max is kept for
-      // both the numerator and the denominator, which leaves O / l unchanged.
-      // The decision is per row (a row that does not move multiplies by exactly
-      // 1), so no row's arithmetic depends on another row's scores; the
-      // wave-wide test only skips the multiplies when no row moves.
-      const bool move = ms > m_run[j] + 8.0f;
-      if (__any(move)) {
-        // (a side effect keeps this a real branch: the compiler would otherwise
-        // hoist the multiplies, which are an identity when no row moves)
-        asm volatile("; rescale" ::: "memory");
-        const float alpha = move ? __builtin_amdgcn_exp2f(m_run[j] - ms) : 1.0f;
-        m_run[j] = move ? ms : m_run[j];
-        l_run[j] *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < HD / 32; ++mb) oacc[j][mb] *= alpha;
-      }
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        t[i] = __builtin_amdgcn_exp2f(ALIBI ? t[i] - m_run[j] : fmaf(t[i], c2, -m_run[j]));
-        lsum += t[i];
-      }
-      l_run[j] += lsum;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        pb[j][u] = as_bf16x8(make_uint4(pack_bf16x2(t[8 * u + 0], t[8 * u + 1]), pack_bf16x2(t[8 * u + 2], t[8 * u + 3]),
-                                        pack_bf16x2(t[8 * u + 4], t[8 * u + 5]), pack_bf16x2(t[8 * u + 6], t[8 * u + 7])));
+    for (int i = 0; i < NR - kKAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // O^T += V^T P^T over four 16-key steps. P^T (the B operand) comes straight
-    // from the probabilities; V^T is read with transposing loads: source lane i
-    // of a 16-lane group points at key row 16u + 8hf + i/4 (+4), columns
-    // d0 + 4(i%4), and lane i then holds V[those 4 keys][d0 + i].
+    __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
+  }
+
+  // O^T += V^T P^T over four 16-key steps of the V tile at vb. V^T is read
+  // with transposing loads: source lane i of a 16-lane group points at key row
+  // 16u + 8hf + i/4 (+4), columns d0 + 4(i%4), and lane i then holds
+  // V[those 4 keys][d0 + i].
+  __device__ __forceinline__ void pv(LdsBytes vb, const bf16x8 (&p)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int mb = 0; mb < HD / 32; ++mb) {
-        LdsBytes p = kb + vtr[mb] + 16 * u * HD * 2;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p + 4 * HD * 2));
+        LdsBytes q = vb + vtr[mb] + 16 * u * HD * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)q);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(q + 4 * HD * 2));
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int j = 0; j < QB; ++j)
-          if (live[j]) oacc[j][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[j][u], oacc[j][mb], 0, 0, 0);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[u], oacc[mb], 0, 0, 0);
       }
     }
   }
+
+  // Online softmax of the tile whose scores are sa, sb (keys k0 .. k0+63),
+  // interleaved with the V^T product of the previous tile (V tile at vprev,
+  // operands pprev): the two are independent, so the vector ALU works while
+  // the matrix core runs. The previous product enters O before O is rescaled
+  // for this tile's max, so O and l stay at the same reference max.
+  template <bool MASK>
+  __device__ __forceinline__ void softmax_pv(const f32x16& sa, const f32x16& sb, int k0, LdsBytes vprev) {
+    const int hf = lane >> 5;
+    // Without ALiBi t keeps the raw scores (the max commutes with the positive
+    // scale, which is folded into the exponent's FMA); with ALiBi t is the
+    // scaled, biased score in log2 units.
+    float t[32];
+    const int dbase = k0 + 8 * hf - qi;  // key - query at register offset 0
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float x = i < 16 ? sa[i] : sb[i - 16];
+      if constexpr (ALIBI) {
+        const float dk = (float)(dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8));
+        t[i] = fmaf(x, c2, slope2 * (CAUSAL ? dk : -fabsf(dk)));
+      } else {
+        t[i] = x;
+      }
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int dk = dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
+        const bool vis = (dk + qi < T) && (!CAUSAL || dk <= 0);
+        t[i] = vis ? t[i] : -INFINITY;
+      }
+    }
+    float mx = t[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, t[i]);
+    mx = fmaxf(mx, xhalf(mx));
+    const float ms = ALIBI ? mx : mx * c2;  // tile max in log2 units
+    // Lazy rescale: a row's running max only moves when its tile max exceeds
+    // it by more than 8 (a factor 2^8); otherwise the stale max is kept for
+    // both the numerator and the denominator, which leaves O / l unchanged.
+    // The decision is per row (a row that does not move multiplies by exactly
+    // 1), so no row's arithmetic depends on another row's scores.
+    const bool move = ms > m_run + 8.0f;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - ms) : 1.0f;
+    m_run = move ? ms : m_run;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      t[i] = __builtin_amdgcn_exp2f(ALIBI ? t[i] - m_run : fmaf(t[i], c2, -m_run));
+      ls[i % 4] += t[i];
+    }
+    l_run = fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+    bf16x8 pnew[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pnew[u] = as_bf16x8(make_uint4(pack_bf16x2(t[8 * u + 0], t[8 * u + 1]), pack_bf16x2(t[8 * u + 2], t[8 * u + 3]),
+                                     pack_bf16x2(t[8 * u + 4], t[8 * u + 5]), pack_bf16x2(t[8 * u + 6], t[8 * u + 7])));
+    pv(vprev, pprev);
+#if defined(__HIP_DEVICE_COMPILE__)
+    // The probabilities are needed only after the rescale branch below; pin
+    // them here so that the compiler does not sink the softmax past the branch
+    // (out of reach of the interleaving).
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pnew[u])));
+    asm volatile("" ::"v"(l_run));
+#endif
+    // Issue order: the first two V^T operands, then per MFMA a slice of the
+    // softmax and the next operand.
+    constexpr int NM = 4 * (HD / 32);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    if (__any(move)) {
+      // (a side effect keeps this a real branch: the compiler would otherwise
+      // hoist the multiplies, which are an identity when no row moves)
+      asm volatile("; rescale" ::: "memory");
+#pragma unroll
+      for (int mb = 0; mb < HD / 32; ++mb) oacc[mb] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pprev[u] = pnew[u];
+  }
 };
 
-// QB = query blocks of 32 rows per wave: QB = 1 runs two waves per SIMD, QB = 2
-// one (its state needs ~400 VGPRs).
-template <int QB>
-struct Sched {
-  static constexpr int WAVES_PER_EU = QB == 2 ? 1 : 2;
-};
-
-template <int HD, bool ALIBI, bool CAUSAL, bool OUT_BF16, int QB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Sched<QB>::WAVES_PER_EU, Sched<QB>::WAVES_PER_EU)))
+template <int HD, bool ALIBI, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using C = Cfg<HD>;
-  // Two stage buffers as separate LDS objects: the compiler then knows that the
-  // DMA filling one stage cannot alias the reads of the other, and does not
-  // wait for the in-flight tile before reading the current one.
+  // Three stage buffers, each its own LDS object: stage kt%3 holds tile kt
+  // (K then V), stage (kt+1)%3 receives tile kt+1 by DMA, stage (kt-1)%3 still
+  // holds V of tile kt-1 for its deferred V^T product. As separate objects the
+  // compiler can tell that the DMA into one stage cannot alias the reads of
+  // another, and does not wait for the in-flight tile before reading.
   __shared__ __attribute__((aligned(16))) unsigned char s0[C::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char s1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char s2[C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -355,7 +371,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
 
   const int head = kvh * a.group + hc * gm.hpw + (wave % gm.hpw);
   const int q0 = qb * gm.bm;
-  const int qw0 = q0 + 32 * QB * (wave / gm.hpw);
+  const int qw0 = q0 + 32 * (wave / gm.hpw);
   const bool wave_active = qw0 < a.T;
 
   const long kvoff = ((long)b * a.KV + kvh) * (long)a.T * HD;
@@ -368,26 +384,29 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   Dma<HD> dma;
   dma.init(wave, lane);
   dma.issue(Kg, Vg, 0, a.T, s0, wave);
+  // Stage 2 stands in for "tile -1": its V part is zeroed and the pending
+  // probabilities start at zero, so the first tile's deferred product adds
+  // exact zeros.
+  for (int e = tid; e < C::V_BYTES / 16; e += NT) reinterpret_cast<uint4*>(s2 + C::K_BYTES)[e] = make_uint4(0, 0, 0, 0);
 
-  WaveState<HD, ALIBI, CAUSAL, QB> ws;
+  WaveState<HD, ALIBI, CAUSAL> ws;
   ws.qi = qw0 + n;
   ws.T = a.T;
   ws.lane = lane;
   ws.init_offsets();
   ws.c2 = a.scale_log2;
   ws.slope2 = ALIBI ? alibi_slope(a.alibi, head, a.H) * 1.4426950408889634f : 0.f;
+  ws.m_run = -INFINITY;
+  ws.l_run = 0.f;
 #pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    ws.m_run[j] = -INFINITY;
-    ws.l_run[j] = 0.f;
+  for (int mb = 0; mb < HD / 32; ++mb) ws.oacc[mb] = f32x16{};
 #pragma unroll
-    for (int mb = 0; mb < HD / 32; ++mb) ws.oacc[j][mb] = f32x16{};
-  }
+  for (int u = 0; u < 4; ++u) ws.pprev[u] = as_bf16x8(make_uint4(0, 0, 0, 0));
 
   // ---- Q rows -> B operands (rotated in fp32, rounded to bf16). When it fits
-  // in the stage-1 area, the rotary cos/sin of the workgroup's bm rows are
-  // computed once (layout [pair][row], so lanes reading consecutive rows hit
-  // distinct banks) and shared by the waves of all heads in the workgroup.
+  // in stage 1, the rotary cos/sin of the workgroup's bm rows are computed once
+  // (layout [pair][row], so lanes reading consecutive rows hit distinct banks)
+  // and shared by the waves of all heads in the workgroup.
   {
     const bool table = a.rope && (HD / 2) * gm.bm * (int)sizeof(float2) <= C::STAGE;
     float2* cs = reinterpret_cast<float2*>(s1);  // [HD/2][bm]
@@ -419,103 +438,113 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       }
       return as_bf16x8(make_uint4(d[0], d[1], d[2], d[3]));
     };
+    const int qr = ws.qi;
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                      (((long)b * a.H + head) * a.T + min(qr, a.T - 1)) * HD);
+    uint4 raw[HD / 16];
 #pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      const int qr = ws.qi + 32 * j;
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                        (((long)b * a.H + head) * a.T + min(qr, a.T - 1)) * HD);
-      uint4 raw[HD / 16];
+    for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
+    if (!a.rope) {
 #pragma unroll
-      for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
-      if (!a.rope) {
+      for (int s = 0; s < HD / 16; ++s) ws.qf[s] = as_bf16x8(raw[s]);
+    } else {
 #pragma unroll
-        for (int s = 0; s < HD / 16; ++s) ws.qf[j][s] = as_bf16x8(raw[s]);
-      } else if (table) {
-#pragma unroll
-        for (int s = 0; s < HD / 16; ++s) ws.qf[j][s] = rotate(raw[s], qr, 8 * s + 4 * hf);
-      } else {
-#pragma unroll
-        for (int s = 0; s < HD / 16; ++s) ws.qf[j][s] = rotate(raw[s], qr, 8 * s + 4 * hf);
-      }
+      for (int s = 0; s < HD / 16; ++s) ws.qf[s] = rotate(raw[s], qr, 8 * s + 4 * hf);
     }
   }
-  // Tile 0 has landed and no wave still reads the table area (stage 1).
+  // Tile 0 has landed, stage 2 is zeroed and no wave still reads the table (stage 1).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // Tiles [0, kt_clean) need no mask for any row of the workgroup: every key is
   // at or before the first query row (causal) and inside the sequence.
   const int kt_clean = min(nkt, CAUSAL ? min((q0 + 1) / BN, a.T / BN) : a.T / BN);
-  // Double buffer: tile kt+1 streams into the other stage while tile kt is
-  // computed; the wait + barrier at the end publishes it and retires stage kt.
-  // The stage parity is a compile-time constant of each step.
-  using Even = std::integral_constant<int, 0>;
-  using Odd = std::integral_constant<int, 1>;
-  auto step = [&](int kt, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
+  // Per tile: start the DMA of tile kt+1, the scores of tile kt, then its
+  // softmax under the deferred V^T product of tile kt-1; the wait + barrier at
+  // the end publishes tile kt+1 and retires stage kt-1.
+  bool pending = true;  // pprev still owes its V^T product
+  auto step = [&](int kt, auto mask_tag, auto phase_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int P = decltype(par_tag)::value;
-    unsigned char* cur = P ? s1 : s0;
-    unsigned char* nxt = P ? s0 : s1;
+    constexpr int P = decltype(phase_tag)::value;
+    unsigned char* cur = P == 0 ? s0 : (P == 1 ? s1 : s2);
+    unsigned char* prv = P == 0 ? s2 : (P == 1 ? s0 : s1);
+    unsigned char* nxt = P == 0 ? s1 : (P == 1 ? s2 : s0);
     const int k0 = kt * BN;
     if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.T, nxt, wave);
-    const bool run = wave_active && !(MASK && CAUSAL && k0 > qw0 + 32 * QB - 1);
-    if (run) ws.template tile<MASK>((LdsBytes)cur, k0);
+    // in a masked tile a wave may be past its last visible key
+    const bool run = wave_active && !(MASK && CAUSAL && k0 > qw0 + 31);
+    if (run) {
+      f32x16 sa, sb;
+      ws.scores((LdsBytes)cur, sa, sb);
+      // A wave in its softmax + deferred-product phase gets issue priority
+      // over a wave computing scores (measured: fewer cycles per tile).
+      __builtin_amdgcn_s_setprio(1);
+      ws.template softmax_pv<MASK>(sa, sb, k0, (LdsBytes)(prv + C::K_BYTES));
+      __builtin_amdgcn_s_setprio(0);
+    } else if (MASK && wave_active && pending) {
+      ws.pv((LdsBytes)(prv + C::K_BYTES), ws.pprev);
+      pending = false;
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
+  using F = std::integral_constant<bool, false>;
+  using M = std::integral_constant<bool, true>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  // Clean tiles in whole rounds of the 3-stage ring; the masked phase (plus at
+  // most two clean tiles) then starts again at stage 0.
+  const int kt3 = kt_clean - kt_clean % 3;
   int kt = 0;
-  auto phase = [&](int end, auto mask_tag) __attribute__((always_inline)) {
-    if (kt & 1) {
-      while (kt < end) {
-        step(kt++, mask_tag, Odd{});
-        if (kt >= end) break;
-        step(kt++, mask_tag, Even{});
-      }
-    } else {
-      while (kt < end) {
-        step(kt++, mask_tag, Even{});
-        if (kt >= end) break;
-        step(kt++, mask_tag, Odd{});
-      }
-    }
-  };
-  phase(kt_clean, std::integral_constant<bool, false>{});
-  phase(nkt, std::integral_constant<bool, true>{});
-
-  if (!wave_active) return;
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    const float l_tot = ws.l_run[j] + xhalf(ws.l_run[j]);
-    const int qi = ws.qi + 32 * j;
-    if (qi >= a.T) continue;
-    const float inv_l = 1.0f / l_tot;
-    const long orow = (((long)b * a.H + head) * a.T + qi) * HD;
-#pragma unroll
-    for (int mb = 0; mb < HD / 32; ++mb) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * mb + 8 * g4 + 4 * hf;
-        const float o0 = ws.oacc[j][mb][4 * g4 + 0] * inv_l, o1 = ws.oacc[j][mb][4 * g4 + 1] * inv_l;
-        const float o2 = ws.oacc[j][mb][4 * g4 + 2] * inv_l, o3 = ws.oacc[j][mb][4 * g4 + 3] * inv_l;
-        if constexpr (OUT_BF16) {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d) =
-              make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + d) = make_float4(o0, o1, o2, o3);
-        }
-      }
-    }
-    if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.T + qi] = (ws.m_run[j] + log2f(l_tot)) * 0.69314718055994531f;
+  for (; kt < kt3; kt += 3) {
+    step(kt, F{}, P0{});
+    step(kt + 1, F{}, P1{});
+    step(kt + 2, F{}, P2{});
   }
-}
+  while (kt < nkt) {
+    step(kt, M{}, P0{});
+    if (++kt >= nkt) break;
+    step(kt, M{}, P1{});
+    if (++kt >= nkt) break;
+    step(kt, M{}, P2{});
+    ++kt;
+  }
+  if (!wave_active) return;
+  // the last tile's V^T product (no DMA is in flight any more)
+  if (pending) {
+    const int p = (nkt - 1) % 3;
+    ws.pv((LdsBytes)((p == 0 ? s0 : (p == 1 ? s1 : s2)) + C::K_BYTES), ws.pprev);
+  }
 
-constexpr int kQB = 1;  // query blocks of 32 rows per wave in the launched kernels
+  const float l_tot = ws.l_run + xhalf(ws.l_run);
+  const int qi = ws.qi;
+  if (qi >= a.T) return;
+  const float inv_l = 1.0f / l_tot;
+  const long orow = (((long)b * a.H + head) * a.T + qi) * HD;
+#pragma unroll
+  for (int mb = 0; mb < HD / 32; ++mb) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * mb + 8 * g4 + 4 * hf;
+      const float o0 = ws.oacc[mb][4 * g4 + 0] * inv_l, o1 = ws.oacc[mb][4 * g4 + 1] * inv_l;
+      const float o2 = ws.oacc[mb][4 * g4 + 2] * inv_l, o3 = ws.oacc[mb][4 * g4 + 3] * inv_l;
+      if constexpr (OUT_BF16) {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + d) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  }
+  if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.T + qi] = (ws.m_run + log2f(l_tot)) * 0.69314718055994531f;
+}
 
 GridMap make_grid(const PrefillArgs& a) {
   GridMap gm;
   gm.hpw = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
   gm.hchunks = a.group / gm.hpw;
-  gm.bm = 32 * kQB * (NW / gm.hpw);
+  gm.bm = 32 * (NW / gm.hpw);
   gm.nqb = (a.T + gm.bm - 1) / gm.bm;
   gm.units = a.B * a.KV * gm.hchunks;
   gm.xcd_aware = (gm.units % 8) == 0;
@@ -525,9 +554,9 @@ GridMap make_grid(const PrefillArgs& a) {
 template <int HD, bool ALIBI, bool CAUSAL>
 void launch_out(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
   if (a.out_bf16) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, true, kQB>), grid, dim3(NT), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, true>), grid, dim3(NT), 0, s, a, gm);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, false, kQB>), grid, dim3(NT), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, false>), grid, dim3(NT), 0, s, a, gm);
   }
 }
 
