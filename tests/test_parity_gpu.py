@@ -95,6 +95,12 @@ SHAPES = [
     (1, 70, 2, 1, 16),
     (1, 129, 4, 2, 32),
     (1, 257, 32, 8, 128),
+    # several query blocks per head: clean tiles, then a masked phase that
+    # starts part-way through the stage ring (8-wave workgroups: 256, 128 and
+    # 64 query rows per head for 1, 2 and 4 heads per key/value head)
+    (1, 700, 4, 4, 128),
+    (1, 600, 8, 4, 64),
+    (1, 1000, 8, 2, 128),
 ]
 
 
@@ -245,6 +251,29 @@ def test_decode_full_size_sampled():
     got = to64(out[pick])
     assert np.abs(got - ref).max() <= 1e-2
     assert np.abs(to64(lse[pick]) - ref_lse).max() <= 2e-2
+
+
+def test_decode_long_split_path():
+    """Enough sequences x KV heads that the launcher picks its longer split: lengths at and
+    around both split sizes, checked on a sample of sequences (and every special length)."""
+    B, H, KV, hd, Lmax = 64, 16, 8, 64, 2100
+    special = [0, 1, 511, 512, 513, 1023, 1024, 1025, 2047, 2048, Lmax - 1]
+    lens = np.random.default_rng(77).integers(0, Lmax, size=B).astype(np.int32)
+    lens[:len(special)] = special
+    w = W.DecodeWorkload("decode-long-split", B, H, KV, hd, 0, 0, 45, 46, 10000.0)
+    inp = W.decode_inputs(w, lens=lens, lmax=Lmax)
+    print(f"[decode long split] B={B} H={H} KV={KV} hd={hd} Lmax={Lmax}", flush=True)
+    out, lse, kc, vc = gpu_decode(inp, w.rope_base, alibi=1)
+    assert torch.isfinite(out).all().item()
+    pick = list(range(len(special))) + [20, 41, 63]
+    ref, ref_lse, ks, vs = attention_decode(to64(inp.q[pick]), to64(inp.k_new[pick]), to64(inp.v_new[pick]),
+                                            to64(inp.k_cache[pick]), to64(inp.v_cache[pick]), lens[pick],
+                                            rope_base=w.rope_base, alibi=1)
+    assert np.abs(to64(out[pick]) - ref).max() <= 1e-2
+    assert np.abs(to64(lse[pick]) - ref_lse).max() <= 2e-2
+    for i, b in enumerate(pick):
+        L = int(lens[b])
+        assert np.array_equal(to64(vc[b, :, L]), vs[i])
 
 
 def test_incremental_decode_equals_prefill():

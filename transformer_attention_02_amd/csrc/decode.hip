@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_split_valu_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- MFMA split kernel
 // bf16, hd in {64, 128}, group = H/KV <= 16. Grid (KV*B, nsplit), 4 waves,
-// kSplitMfma key slots per workgroup.
+// kSplitMfma (or kSplitMfmaLong) key slots per workgroup.
 // The group's query heads are the columns of S^T = K Q^T computed with
 // v_mfma_f32_16x16x32_bf16, so each K/V byte is read from memory once for all of
 // them. Each wave streams 32-key tiles (interleaved with the other waves) through
@@ -148,7 +148,6 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;  // keys per wave tile
 constexpr int kWaves = 4;
-constexpr int kTilesPerWave = kSplitMfma / (kWaves * kTile);
 
 // MFMA row rho (0..15) of key block kb (0 or 1) holds tile key 8*(rho/4) + 4*kb + rho%4.
 __device__ __forceinline__ int kperm16(int rho, int kb) { return ((rho >> 2) << 3) | (kb << 2) | (rho & 3); }
@@ -170,9 +169,10 @@ __device__ __forceinline__ int dv_off(int r, int c) {  // V tile: 16-byte chunk 
   }
 }
 
-template <int HD>
+template <int HD, int TPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_mfma_kernel(DecodeArgs a) {
+  constexpr int SPLIT = kWaves * kTile * TPW;  // key slots per workgroup
   constexpr int KCH = HD / 8;                 // 16-byte chunks per row
   constexpr int TILE_BYTES = kTile * HD * 2;  // one K or V tile
   constexpr int LOADS = kTile * KCH / 64;     // 16-byte loads per lane per tensor
@@ -187,13 +187,40 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   const int L = a.lens[b];
   if (bad_len(L, a.Lmax)) return;
   const int nk = L + 1;
-  const int k0 = sp * kSplitMfma;
+  const int k0 = sp * SPLIT;
   if (k0 >= nk) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
   const int G = a.group;
   const bool qcol = n < G;
   const int head = kvh * G + (qcol ? n : 0);
+
+  const long cbase = ((long)b * a.KV + kvh) * (long)a.Lmax * HD;
+  const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k_cache) + cbase;
+  const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v_cache) + cbase;
+  unsigned char* kl = smem + wave * 2 * TILE_BYTES;
+  unsigned char* vl = kl + TILE_BYTES;
+
+  // Two tiles of K/V in flight per wave: slot t&1 holds tile t until it is
+  // written to LDS, then receives tile t+2. The first two go out before the
+  // rotary table and the query set-up, which then hide under their latency.
+  // Buffer descriptors start at the tile and end at key slot nk, so rows past
+  // the sequence end read as zero. (The wave whose tile covers slot L may read
+  // it before the new key lands there; it patches that row in LDS.)
+  uint4 kr[2][LOADS], vr[2][LOADS];
+  auto load_tile = [&](int slot, int ts) {
+    const int bytes = (nk - ts) * HD * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)ts * HD, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)ts * HD, bytes);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      kr[slot][i] = buffer_load16_stream(rk, 16 * (lane + 64 * i));
+      vr[slot][i] = buffer_load16_stream(rv, 16 * (lane + 64 * i));
+    }
+  };
+  const auto tile_start = [&](int t) { return k0 + (t * kWaves + wave) * kTile; };
+  if (tile_start(0) < nk) load_tile(0, tile_start(0));
+  if (TPW > 1 && tile_start(1) < nk) load_tile(1, tile_start(1));
 
   // cos/sin of the rotary angle at position L for every pair, shared in LDS.
   __shared__ float2 cs_tab[HD / 2];
@@ -205,7 +232,7 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   // This split holds the new token's slot L: its workgroup writes the rotated
   // key and the value to the cache, and the wave whose tile covers slot L
   // patches that row of its LDS tile (it never reads slot L back from memory).
-  const bool own_slot = L >= k0 && L < k0 + kSplitMfma;
+  const bool own_slot = L >= k0 && L < k0 + SPLIT;
   uint32_t knew = 0, vnew = 0;  // lane p < HD/2: pair p of R(L) k_new and v_new (bf16x2)
   const long cslot = (((long)b * a.KV + kvh) * a.Lmax + L) * HD;
   const long nslot = ((long)b * a.KV + kvh) * HD;
@@ -245,37 +272,13 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   const float c2 = a.scale_log2;
   const float slope2 = a.alibi ? alibi_slope(a.alibi, head, a.H) * kLog2e : 0.f;
 
-  const long cbase = ((long)b * a.KV + kvh) * (long)a.Lmax * HD;
-  const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k_cache) + cbase;
-  const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v_cache) + cbase;
-  unsigned char* kl = smem + wave * 2 * TILE_BYTES;
-  unsigned char* vl = kl + TILE_BYTES;
-
   f32x4_t oacc[HD / 16];
 #pragma unroll
   for (int db = 0; db < HD / 16; ++db) oacc[db] = f32x4_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Two tiles of K/V in flight per wave: slot t&1 holds tile t until it is
-  // written to LDS, then receives tile t+2. Buffer descriptors start at the tile
-  // and end at key slot nk, so rows past the sequence end read as zero.
-  uint4 kr[2][LOADS], vr[2][LOADS];
-  auto load_tile = [&](int slot, int ts) {
-    const int bytes = (nk - ts) * HD * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)ts * HD, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)ts * HD, bytes);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      kr[slot][i] = buffer_load16(rk, 16 * (lane + 64 * i));
-      vr[slot][i] = buffer_load16(rv, 16 * (lane + 64 * i));
-    }
-  };
-  const auto tile_start = [&](int t) { return k0 + (t * kWaves + wave) * kTile; };
-  if (tile_start(0) < nk) load_tile(0, tile_start(0));
-  if (kTilesPerWave > 1 && tile_start(1) < nk) load_tile(1, tile_start(1));
-
-#pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     const int ts = tile_start(t);
     if (ts >= nk) break;
     const int slot = t & 1;
@@ -291,7 +294,7 @@ void decode_split_mfma_kernel(DecodeArgs a) {
       *reinterpret_cast<uint32_t*>(kl + dk_off<HD>(r, lane >> 2) + 4 * (lane & 3)) = knew;
       *reinterpret_cast<uint32_t*>(vl + dv_off<HD>(r, lane >> 2) + 4 * (lane & 3)) = vnew;
     }
-    if (t + 2 < kTilesPerWave && tile_start(t + 2) < nk) load_tile(slot, tile_start(t + 2));
+    if (t + 2 < TPW && tile_start(t + 2) < nk) load_tile(slot, tile_start(t + 2));
 
     // S^T = K Q^T for the tile's two 16-key blocks
     f32x4_t sacc[2];
@@ -466,7 +469,11 @@ template <int BF16, int HD>
 hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHook& tm) {
   DecodeArgs a = a0;
   const bool mfma = decode_mfma_supported(a, BF16);
-  a.split = mfma ? kSplitMfma : kDecodeSplit;
+  // MFMA path: the longer split when it still gives at least four workgroups
+  // per CU (measured on the 64-sequence, 8-KV-head cache: 5.6 -> 6.0 TB/s), so
+  // the per-workgroup set-up is amortised over more keys.
+  const bool long_split = (long)a.KV * a.B * ((a.Lmax + kSplitMfmaLong - 1) / kSplitMfmaLong) >= 1024;
+  a.split = mfma ? (long_split ? kSplitMfmaLong : kSplitMfma) : kDecodeSplit;
   a.nsplit = (a.Lmax + a.split - 1) / a.split;
   hipError_t e = hipSuccess;
   if (!mfma) {  // the MFMA split kernel appends the new token itself
@@ -476,7 +483,12 @@ hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHoo
   if ((e = tm.before(s)) != hipSuccess) return e;
   if (mfma) {
     if constexpr (HD == 64 || HD == 128) {
-      hipLaunchKernelGGL((decode_split_mfma_kernel<HD>), dim3(a.KV * a.B, a.nsplit), dim3(256), 0, s, a);
+      constexpr int TPW = kSplitMfma / (kWaves * kTile);
+      if (a.split == kSplitMfmaLong) {
+        hipLaunchKernelGGL((decode_split_mfma_kernel<HD, 2 * TPW>), dim3(a.KV * a.B, a.nsplit), dim3(256), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((decode_split_mfma_kernel<HD, TPW>), dim3(a.KV * a.B, a.nsplit), dim3(256), 0, s, a);
+      }
     }
   } else {
     hipLaunchKernelGGL((decode_split_valu_kernel<BF16, HD>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, s, a);
