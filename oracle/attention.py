@@ -30,6 +30,15 @@ What is computed (all in fp64 from the exact values the GPU receives):
   0..L-1 (already rotated) plus its own key rotated at L (lab Exercise 2: the
   incremental result must equal the full computation; "Building Grouped-Query
   Attention ...", roadmap item on a pre-allocated cache written by position).
+* Chunked prefill: a chunk of Tq queries that are tokens q_offset ..
+  q_offset+Tq-1 of a key sequence of Tk tokens (the chunk's own keys included)
+  attends with the same causal test on token indices. Processing a prompt
+  chunk by chunk must reproduce the full computation (lab Exercise 2 with
+  chunks instead of single tokens).
+* Sliding window (the lab's Exercise 3, and the sliding-window mode on the
+  roadmap of "Building Grouped-Query Attention ..."): with a window of W tokens
+  the query at token i sees keys j with i - W < j <= i, i.e. itself and the
+  W - 1 tokens before it.
 
 The tiled online softmax that the GPU runs is an exact rearrangement of this
 definition (the recurrences of "Building a Transformer from Scratch", Part 3,
@@ -95,11 +104,13 @@ def alibi_slopes(H: int, kind: int) -> np.ndarray:
     raise ValueError(f"unknown ALiBi kind {kind}")
 
 
-def _attend(qr, kr, v, q_idx, k_idx, causal, slope, scale):
+def _attend(qr, kr, v, q_idx, k_idx, causal, slope, scale, window=0):
     """Softmax attention of rotated query rows ``qr`` [n, hd] over keys ``kr`` [m, hd].
 
-    ``q_idx``/``k_idx`` are the token indices used for the causal test and the
-    ALiBi distance. Returns (out [n, hd], lse [n]) with lse = log sum_j exp(s_ij).
+    ``q_idx``/``k_idx`` are the token indices used for the causal test, the
+    sliding window (``window`` > 0: keys within the last ``window`` tokens up to
+    and including the query's) and the ALiBi distance. Returns (out [n, hd],
+    lse [n]) with lse = log sum_j exp(s_ij) over the visible keys.
     """
     s = (qr @ kr.T) * scale                                   # [n, m]
     dist = q_idx[:, None].astype(np.float64) - k_idx[None, :].astype(np.float64)
@@ -110,6 +121,8 @@ def _attend(qr, kr, v, q_idx, k_idx, causal, slope, scale):
     for r in range(qr.shape[0]):
         row = s[r]
         vis = (k_idx <= q_idx[r]) if causal else np.ones(len(k_idx), dtype=bool)
+        if window:
+            vis &= k_idx > q_idx[r] - window
         sv = row[vis]
         m = sv.max()
         e = np.exp(sv - m)
@@ -120,11 +133,14 @@ def _attend(qr, kr, v, q_idx, k_idx, causal, slope, scale):
 
 
 def attention_prefill(q, k, v, *, pos0: int = 0, rope_base: float = 10000.0, causal: bool = True,
-                      alibi: int = ALIBI_NONE, rows=None):
-    """Attention forward over a whole sequence.
+                      alibi: int = ALIBI_NONE, rows=None, q_offset: int = 0, window: int = 0):
+    """Attention forward over a sequence, or over a chunk of its queries.
 
-    q [B,H,T,hd]; k, v [B,KV,T,hd] (pre-rotation). Query and key t sit at
-    position pos0 + t. Returns (out [B,H,T,hd], lse [B,H,T]) in fp64.
+    q [B,H,Tq,hd]; k, v [B,KV,Tk,hd] (pre-rotation). Key token j sits at
+    position pos0 + j; query row i is token q_offset + i (position
+    pos0 + q_offset + i), and q_offset + Tq <= Tk (the chunk's own keys are part
+    of k). ``window`` > 0 (causal only) limits each query to its last
+    ``window`` tokens. Returns (out [B,H,Tq,hd], lse [B,H,Tq]) in fp64.
 
     ``rows`` optionally restricts the computation to a list of (b, h, i)
     triples; the result is then (out [n, hd], lse [n]) in that order.
@@ -132,15 +148,20 @@ def attention_prefill(q, k, v, *, pos0: int = 0, rope_base: float = 10000.0, cau
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    B, H, T, hd = q.shape
-    KV = k.shape[1]
+    B, H, Tq, hd = q.shape
+    KV, Tk = k.shape[1], k.shape[2]
     if H % KV:
         raise ValueError("query heads must be a multiple of key/value heads")
+    if q_offset < 0 or q_offset + Tq > Tk:
+        raise ValueError("the query chunk must lie inside the key sequence")
+    if window < 0 or (window and not causal):
+        raise ValueError("a sliding window needs causal attention and a positive width")
     group = H // KV
     scale = 1.0 / math.sqrt(hd)
     slopes = alibi_slopes(H, alibi)
-    positions = pos0 + np.arange(T)
-    idx = np.arange(T)
+    positions = pos0 + np.arange(Tk)
+    idx = np.arange(Tk)
+    q_tok = q_offset + np.arange(Tq)
 
     if rows is not None:
         rows = [tuple(int(t) for t in r) for r in rows]
@@ -152,22 +173,22 @@ def attention_prefill(q, k, v, *, pos0: int = 0, rope_base: float = 10000.0, cau
         for (b, h), lst in by_head.items():
             g = h // group
             qi = np.array([i for _, i in lst])
-            qr = apply_rope(q[b, h, qi], positions[qi], rope_base)
+            qr = apply_rope(q[b, h, qi], positions[q_tok[qi]], rope_base)
             kr = apply_rope(k[b, g], positions, rope_base)
-            o, l = _attend(qr, kr, v[b, g], qi, idx, causal, slopes[h], scale)
+            o, l = _attend(qr, kr, v[b, g], q_tok[qi], idx, causal, slopes[h], scale, window)
             for j, (n, _) in enumerate(lst):
                 out[n] = o[j]
                 lse[n] = l[j]
         return out, lse
 
-    out = np.empty((B, H, T, hd))
-    lse = np.empty((B, H, T))
+    out = np.empty((B, H, Tq, hd))
+    lse = np.empty((B, H, Tq))
     for b in range(B):
         for g in range(KV):
             kr = apply_rope(k[b, g], positions, rope_base)
             for h in range(g * group, (g + 1) * group):
-                qr = apply_rope(q[b, h], positions, rope_base)
-                out[b, h], lse[b, h] = _attend(qr, kr, v[b, g], idx, idx, causal, slopes[h], scale)
+                qr = apply_rope(q[b, h], positions[q_tok], rope_base)
+                out[b, h], lse[b, h] = _attend(qr, kr, v[b, g], q_tok, idx, causal, slopes[h], scale, window)
     return out, lse
 
 

@@ -38,12 +38,14 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 # ---------------------------------------------------------------- brute force
-def brute_attention(q, k, v, pos0, base, causal, alibi):
+def brute_attention(q, k, v, pos0, base, causal, alibi, q_offset=0, window=0):
     """Scalar loops. RoPE as multiplication of (x0 + i x1) by e^{i p theta}
     (the complex form of the RoPE equation on the transformer-from-scratch page);
-    the softmax as exp / fsum without max subtraction; heads grouped by repetition."""
-    B, H, T, hd = q.shape
-    KV = k.shape[1]
+    the softmax as exp / fsum without max subtraction; heads grouped by repetition.
+    Query row i is token q_offset + i of the key sequence; with a window of W
+    tokens it sees keys q_offset + i - W + 1 .. q_offset + i."""
+    B, H, Tq, hd = q.shape
+    KV, T = k.shape[1], k.shape[2]
     kv_of = [g for g in range(KV) for _ in range(H // KV)]
     if alibi == ALIBI_GEOMETRIC:
         slope = [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
@@ -62,22 +64,23 @@ def brute_attention(q, k, v, pos0, base, causal, alibi):
             outv += [z.real, z.imag]
         return outv
 
-    out = np.zeros((B, H, T, hd))
-    lse = np.zeros((B, H, T))
+    out = np.zeros((B, H, Tq, hd))
+    lse = np.zeros((B, H, Tq))
     for b in range(B):
         for h in range(H):
             g = kv_of[h]
             keys = [rot(k[b, g, j], pos0 + j) for j in range(T)]
-            for i in range(T):
-                qi = rot(q[b, h, i], pos0 + i)
-                js = [j for j in range(T) if (j <= i or not causal)]
+            for r in range(Tq):
+                i = q_offset + r
+                qi = rot(q[b, h, r], pos0 + i)
+                js = [j for j in range(T) if (j <= i or not causal) and (window == 0 or i - j < window)]
                 sc = [math.fsum(a * c for a, c in zip(qi, keys[j])) / math.sqrt(hd) - slope[h] * abs(i - j)
                       for j in js]
                 ex = [math.exp(s) for s in sc]
                 z = math.fsum(ex)
                 for d in range(hd):
-                    out[b, h, i, d] = math.fsum(e * v[b, g, j, d] for e, j in zip(ex, js)) / z
-                lse[b, h, i] = math.log(z)
+                    out[b, h, r, d] = math.fsum(e * v[b, g, j, d] for e, j in zip(ex, js)) / z
+                lse[b, h, r] = math.log(z)
     return out, lse
 
 
@@ -95,6 +98,34 @@ def test_prefill_matches_brute_force(causal, alibi, base, pos0, H, KV):
     ref, ref_lse = brute_attention(q, k, v, pos0, base, causal, alibi)
     assert np.abs(out - ref).max() < 1e-13
     assert np.abs(lse - ref_lse).max() < 1e-13
+
+
+@pytest.mark.parametrize("Tq,Tk,q_offset", [(9, 9, 0), (3, 9, 6), (4, 9, 2), (1, 9, 8), (9, 12, 3)])
+@pytest.mark.parametrize("window", [0, 1, 2, 3, 5, 100])
+@pytest.mark.parametrize("alibi", [ALIBI_NONE, ALIBI_GEOMETRIC])
+def test_chunk_and_window_match_brute_force(Tq, Tk, q_offset, window, alibi):
+    """Chunked queries over a longer key sequence, with and without a sliding window."""
+    rng = np.random.default_rng(hash((Tq, Tk, q_offset, window, alibi)) % 2**32)
+    B, H, KV, hd = 1, 4, 2, 6
+    q = rng.normal(size=(B, H, Tq, hd))
+    k = rng.normal(size=(B, KV, Tk, hd))
+    v = rng.normal(size=(B, KV, Tk, hd))
+    out, lse = attention_prefill(q, k, v, pos0=5, rope_base=10000.0, causal=True, alibi=alibi,
+                                 q_offset=q_offset, window=window)
+    ref, ref_lse = brute_attention(q, k, v, 5, 10000.0, True, alibi, q_offset=q_offset, window=window)
+    assert np.abs(out - ref).max() < 1e-13
+    assert np.abs(lse - ref_lse).max() < 1e-13
+
+
+def test_chunk_and_window_argument_checks():
+    q = np.zeros((1, 2, 4, 4))
+    k = np.zeros((1, 2, 6, 4))
+    with pytest.raises(ValueError):
+        attention_prefill(q, k, k, q_offset=3)             # chunk runs past the keys
+    with pytest.raises(ValueError):
+        attention_prefill(q, k, k, q_offset=-1)
+    with pytest.raises(ValueError):
+        attention_prefill(q, k, k, q_offset=2, window=2, causal=False)
 
 
 # ------------------------------------------------------- library routine (SDPA)
@@ -134,6 +165,29 @@ def test_prefill_matches_torch_sdpa(causal, alibi, base):
     assert np.abs(out - ref.numpy()).max() < 1e-12
 
 
+@pytest.mark.parametrize("window,q_offset", [(0, 0), (4, 0), (0, 19), (7, 19), (1, 25)])
+def test_chunk_and_window_match_torch_sdpa(window, q_offset):
+    """The same routine with an explicit boolean mask for the chunk offset and the window."""
+    g = torch.Generator().manual_seed(12)
+    B, H, KV, Tk, hd = 2, 8, 2, 40, 16
+    Tq = Tk - q_offset
+    q = torch.randn(B, H, Tq, hd, generator=g, dtype=torch.float64)
+    k = torch.randn(B, KV, Tk, hd, generator=g, dtype=torch.float64)
+    v = torch.randn(B, KV, Tk, hd, generator=g, dtype=torch.float64)
+    pos0, base = 2, 10000.0
+    qr = torch_rope(q, pos0 + q_offset, base)
+    kr = torch_rope(k, pos0, base)
+    i = torch.arange(q_offset, q_offset + Tq)[:, None]
+    j = torch.arange(Tk)[None, :]
+    allowed = j <= i
+    if window:
+        allowed &= j > i - window
+    ref = F.scaled_dot_product_attention(qr, kr, v, attn_mask=allowed, enable_gqa=True)
+    out, _ = attention_prefill(q.numpy(), k.numpy(), v.numpy(), pos0=pos0, rope_base=base, causal=True,
+                               q_offset=q_offset, window=window)
+    assert np.abs(out - ref.numpy()).max() < 1e-12
+
+
 # ---------------------------------------------------- the lab page's properties
 def lab_forward(x, pos0, causal=True, rotate_v=False):
     _, Wq, Wk, Wv, Wo = W.lab_instance()
@@ -167,6 +221,77 @@ def test_lab_break_it_on_purpose():
     x2[-1] += 1.0
     assert np.abs(lab_forward(x2, 0, causal=False)[:-1] - lab_forward(x, 0, causal=False)[:-1]).max() > 1e-3
     assert np.abs(lab_forward(x, 100, rotate_v=True) - lab_forward(x, 0, rotate_v=True)).max() > 1e-3
+
+
+def lab_layer(x, window):
+    """One application of the lab's attention (its projections and output
+    projection) with a sliding window of ``window`` tokens."""
+    _, Wq, Wk, Wv, Wo = W.lab_instance()
+    T = x.shape[0]
+    q = W.split_heads(x @ Wq, 4)
+    k = W.split_heads(x @ Wk, 2)
+    v = W.split_heads(x @ Wv, 2)
+    out, _ = attention_prefill(q, k, v, pos0=0, rope_base=10000.0, causal=True, window=window)
+    return out[0].transpose(1, 0, 2).reshape(T, -1) @ Wo
+
+
+def test_lab_sliding_window_exercise():
+    """Exercise 3: with a window of 3 tokens, after two layers the last output
+    can only depend on tokens T-5 .. T-1 (each layer reaches 2 tokens further
+    back); the earlier token must leave it exactly unchanged."""
+    x = W.lab_instance()[0]
+    T = x.shape[0]
+    last = lab_layer(lab_layer(x, 3), 3)[-1]
+    influence = []
+    for t in range(T):
+        x2 = x.copy()
+        x2[t] += 1.0
+        influence.append(np.abs(lab_layer(lab_layer(x2, 3), 3)[-1] - last).max())
+    assert influence[0] == 0.0
+    assert all(d > 1e-6 for d in influence[1:])
+    # one layer reaches two tokens back only
+    one = lab_layer(x, 3)[-1]
+    x3 = x.copy()
+    x3[T - 4] += 1.0
+    assert np.abs(lab_layer(x3, 3)[-1] - one).max() == 0.0
+
+
+def test_chunked_prefill_equals_full_rows():
+    """Processing the prompt chunk by chunk reproduces the full computation (lab
+    Exercise 2 with chunks of several tokens), with and without a window."""
+    rng = np.random.default_rng(21)
+    B, H, KV, T, hd = 2, 4, 2, 23, 8
+    q = rng.normal(size=(B, H, T, hd))
+    k = rng.normal(size=(B, KV, T, hd))
+    v = rng.normal(size=(B, KV, T, hd))
+    for window in (0, 5):
+        full, full_lse = attention_prefill(q, k, v, pos0=4, rope_base=500000.0, alibi=ALIBI_GEOMETRIC,
+                                           window=window)
+        for start, stop in [(0, 7), (7, 8), (8, 23)]:
+            part, part_lse = attention_prefill(q[:, :, start:stop], k[:, :, :stop], v[:, :, :stop], pos0=4,
+                                               rope_base=500000.0, alibi=ALIBI_GEOMETRIC, q_offset=start,
+                                               window=window)
+            assert np.abs(part - full[:, :, start:stop]).max() < 1e-13
+            assert np.abs(part_lse - full_lse[:, :, start:stop]).max() < 1e-13
+
+
+def test_window_closed_forms():
+    """A window of one token returns the token's own value; Q = 0 averages the
+    values of the last W tokens; a window at least as long as the sequence is
+    plain causal attention."""
+    rng = np.random.default_rng(22)
+    B, H, KV, T, hd = 1, 2, 1, 11, 4
+    q = rng.normal(size=(B, H, T, hd))
+    k = rng.normal(size=(B, KV, T, hd))
+    v = rng.normal(size=(B, KV, T, hd))
+    one, lse1 = attention_prefill(q, k, v, window=1)
+    assert np.abs(one - v[:, [0, 0]]).max() < 1e-15
+    zero, _ = attention_prefill(np.zeros_like(q), k, v, window=4)
+    for i in range(T):
+        assert np.abs(zero[0, 0, i] - v[0, 0, max(0, i - 3):i + 1].mean(axis=0)).max() < 1e-14
+    wide, _ = attention_prefill(q, k, v, window=T)
+    causal, _ = attention_prefill(q, k, v)
+    assert np.array_equal(wide, causal)
 
 
 def test_tiny_fp32_inputs_are_the_lab_instance():
