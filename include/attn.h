@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -117,6 +117,39 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
                      int B, int T, int H, int KV, int hd, int pos0, double rope_base,
                      int causal, int alibi, int dtype, int out_dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Chunked prefill and sliding-window attention: the same forward for a chunk
+ * of Tq queries that are tokens q_offset .. q_offset+Tq-1 of a Tk-token key
+ * sequence (a prompt processed chunk by chunk, as lab Exercise 2 of "Write
+ * attention from scratch" does token by token), optionally restricted to a
+ * sliding window of the last `window` tokens (that page's Exercise 3; the
+ * sliding-window mode on the roadmap of "Building Grouped-Query Attention with
+ * RoPE and Flash Attention from Scratch").
+ *
+ *   q    [B, H,  Tq, hd]  dtype, before rotation; row i is token q_offset + i
+ *   k    [B, KV, Tk, hd]  dtype, before rotation (the chunk's own keys are
+ *                         tokens q_offset .. q_offset+Tq-1 of it)
+ *   v    [B, KV, Tk, hd]  dtype
+ *   out  [B, H,  Tq, hd]  out_dtype (written)
+ *   lse  [B, H,  Tq]      fp32 (written); may be NULL
+ *   Key token j sits at position pos0 + j, query row i at pos0 + q_offset + i.
+ *   causal: 1 keeps keys j <= q_offset + i. window > 0 (causal only) keeps
+ *   only keys j > q_offset + i - window, i.e. the query's own token and the
+ *   window - 1 before it; 0 means no window. ALiBi distances are in tokens.
+ *   workspace: at least attn_prefill_workspace_bytes(B, Tk, KV, hd, dtype,
+ *   rope_base) bytes.
+ *
+ * Requires 0 <= q_offset and q_offset + Tq <= Tk (ATTN_ERR_SHAPE otherwise);
+ * window < 0 is ATTN_ERR_SHAPE, window > 0 with causal = 0 ATTN_ERR_UNSUPPORTED.
+ * Keys outside every query's window must still hold finite values (their
+ * zero weights multiply them). attn_prefill_fwd is this call with
+ * Tq = Tk = T, q_offset = 0, window = 0. Other rules as attn_prefill_fwd.
+ */
+int attn_prefill_ex_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int Tq, int Tk, int H, int KV, int hd, int pos0, int q_offset,
+                        int window, double rope_base, int causal, int alibi, int dtype,
+                        int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace attn_decode_fwd needs for its split-KV partials

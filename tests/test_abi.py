@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bd.attn_abi_version() == 1
+    assert bd.attn_abi_version() == 2
     names = {c: bd.attn_status_str(c) for c in range(7)}
     assert names == {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
                      4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP"}
@@ -79,6 +79,33 @@ def _prefill(**kw):
 ])
 def test_prefill_validation(kw, code):
     st = _prefill(**kw)
+    assert st == code, (st, bd.attn_last_error())
+    assert bd.attn_last_error() != ""
+
+
+def _prefill_ex(**kw):
+    args = dict(q=FAKE, k=FAKE2, v=FAKE3, out=FAKE4, lse=None, B=1, Tq=16, Tk=48, H=4, KV=2, hd=64, pos0=0,
+                q_offset=32, window=0, rope_base=10000.0, causal=1, alibi=0, dtype=bd.ATTN_DTYPE_BF16,
+                out_dtype=bd.ATTN_DTYPE_F32, workspace=0x100000, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return bd.attn_prefill_ex_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), bd.ATTN_ERR_NULL),
+    (dict(Tq=0), bd.ATTN_ERR_SHAPE),
+    (dict(Tk=0), bd.ATTN_ERR_SHAPE),
+    (dict(q_offset=-1), bd.ATTN_ERR_SHAPE),
+    (dict(q_offset=33), bd.ATTN_ERR_SHAPE),          # chunk would run past the keys
+    (dict(Tq=49, q_offset=0), bd.ATTN_ERR_SHAPE),
+    (dict(window=-3), bd.ATTN_ERR_SHAPE),
+    (dict(window=8, causal=0), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(hd=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(k=FAKE2 + 4), bd.ATTN_ERR_ALIGN),
+    (dict(workspace_bytes=48 * 2 * 64 * 2 - 2), bd.ATTN_ERR_WORKSPACE),   # rotated keys need Tk rows
+])
+def test_prefill_ex_validation(kw, code):
+    st = _prefill_ex(**kw)
     assert st == code, (st, bd.attn_last_error())
     assert bd.attn_last_error() != ""
 

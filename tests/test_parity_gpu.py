@@ -39,12 +39,13 @@ def gpu_prefill(q, k, v, **kw):
     return out, lse
 
 
-def check_prefill(q, k, v, pos0=0, rope_base=10000.0, causal=True, alibi=0, label=""):
+def check_prefill(q, k, v, pos0=0, rope_base=10000.0, causal=True, alibi=0, label="", q_offset=0, window=0):
     print(f"[prefill] {label} q{tuple(q.shape)} k{tuple(k.shape)} {q.dtype} pos0={pos0} base={rope_base} "
-          f"causal={causal} alibi={alibi}", flush=True)
-    out, lse = gpu_prefill(q, k, v, pos0=pos0, rope_base=rope_base, causal=causal, alibi=alibi)
+          f"causal={causal} alibi={alibi} q_offset={q_offset} window={window}", flush=True)
+    out, lse = gpu_prefill(q, k, v, pos0=pos0, rope_base=rope_base, causal=causal, alibi=alibi, q_offset=q_offset,
+                           window=window)
     ref, ref_lse = attention_prefill(to64(q), to64(k), to64(v), pos0=pos0, rope_base=rope_base,
-                                     causal=causal, alibi=alibi)
+                                     causal=causal, alibi=alibi, q_offset=q_offset, window=window)
     o = to64(out)
     assert np.isfinite(o).all(), "unwritten or non-finite output"
     err = np.abs(o - ref).max()
@@ -129,6 +130,43 @@ def test_prefill_flags(flags, dtype):
     causal, alibi, base, pos0 = flags
     q, k, v = W.random_prefill(7, 2, 190, 8, 2, 128, "bf16" if dtype == torch.bfloat16 else "f32")
     check_prefill(q, k, v, pos0=pos0, rope_base=base, causal=causal, alibi=alibi, label="flags")
+
+
+CHUNKS = [
+    # B, Tq, Tk, H, KV, hd, q_offset, window
+    (1, 300, 300, 8, 2, 128, 0, 64),        # sliding window over a full prompt
+    (1, 300, 300, 8, 2, 128, 0, 1),         # one-token window: every row returns its own value
+    (2, 200, 700, 8, 2, 128, 500, 0),       # last chunk of a prompt, no window
+    (1, 333, 1000, 8, 2, 128, 600, 257),    # middle chunk with a window that starts mid-tile
+    (1, 1, 513, 8, 2, 64, 512, 0),          # a one-token chunk (decode-like)
+    (1, 250, 900, 4, 4, 128, 100, 300),     # MHA: 256-row query blocks, waves skip tiles on both sides
+    (1, 100, 400, 6, 2, 64, 300, 33),       # three heads per KV head
+    (1, 130, 130, 4, 2, 32, 0, 17),         # vector-ALU kernel (hd 32)
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", CHUNKS, ids=lambda c: "B%dTq%dTk%dH%dKV%dhd%d_off%d_w%d" % c)
+def test_prefill_chunk_and_window(shape, dtype):
+    B, Tq, Tk, H, KV, hd, off, win = shape
+    q, k, v = W.random_prefill(2000 + Tk + win, B, Tk, H, KV, hd, "bf16" if dtype == torch.bfloat16 else "f32")
+    q = q[:, :, off:off + Tq].contiguous()
+    check_prefill(q, k, v, pos0=5, rope_base=10000.0, alibi=1 if win % 2 else 0, q_offset=off, window=win,
+                  label="chunk/window")
+
+
+def test_chunked_prefill_equals_full_prefill_bitwise():
+    """Processing the prompt in chunks gives the full call's rows bit for bit (bf16, GQA, window)."""
+    B, T, H, KV, hd = 1, 640, 8, 2, 128
+    q, k, v = W.random_prefill(77, B, T, H, KV, hd)
+    for window in (0, 150):
+        full, full_lse = gpu_prefill(q, k, v, rope_base=10000.0, window=window)
+        for start, stop in [(0, 100), (100, 357), (357, 640)]:
+            part, part_lse = gpu_prefill(q[:, :, start:stop].contiguous(), k[:, :, :stop].contiguous(),
+                                         v[:, :, :stop].contiguous(), rope_base=10000.0, q_offset=start,
+                                         window=window)
+            assert torch.equal(part, full[:, :, start:stop]), (window, start, stop)
+            assert torch.equal(part_lse, full_lse[:, :, start:stop])
 
 
 def test_bf16_output_rounding():

@@ -39,6 +39,7 @@ EXPORTS = (
     "attn_set_timing_events",
     "attn_prefill_workspace_bytes",
     "attn_prefill_fwd",
+    "attn_prefill_ex_fwd",
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
 )
@@ -55,6 +56,8 @@ _SIGS = {
     "attn_set_timing_events": (_I, [_P, _P]),
     "attn_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _D]),
     "attn_prefill_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I, _I, _I, _P, _S, _P]),
+    "attn_prefill_ex_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _D, _I, _I, _I, _I, _P, _S,
+                                 _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I, _P, _S, _P]),
 }
@@ -115,6 +118,13 @@ def attn_prefill_fwd(q, k, v, out, lse, B, T, H, KV, hd, pos0, rope_base, causal
                                    dtype, out_dtype, workspace, workspace_bytes, stream)
 
 
+def attn_prefill_ex_fwd(q, k, v, out, lse, B, Tq, Tk, H, KV, hd, pos0, q_offset, window, rope_base, causal, alibi,
+                        dtype, out_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().attn_prefill_ex_fwd(q, k, v, out, lse, B, Tq, Tk, H, KV, hd, pos0, q_offset, window,
+                                      float(rope_base), causal, alibi, dtype, out_dtype, workspace, workspace_bytes,
+                                      stream)
+
+
 def attn_decode_workspace_bytes(B, H, KV, hd, Lmax) -> int:
     return load().attn_decode_workspace_bytes(B, H, KV, hd, Lmax)
 
@@ -156,31 +166,38 @@ def prefill_workspace(B, T, KV, hd, dtype_code, rope_base, device):
 
 
 def prefill(q, k, v, *, pos0=0, rope_base=10000.0, causal=True, alibi=ATTN_ALIBI_NONE, out_dtype=None,
-            want_lse=True, out=None, lse=None, workspace=None, stream=None):
-    """Run attn_prefill_fwd on torch tensors q [B,H,T,hd], k/v [B,KV,T,hd] (same dtype, contiguous, on GPU).
+            want_lse=True, out=None, lse=None, workspace=None, stream=None, q_offset=0, window=0):
+    """Run the prefill forward on torch tensors q [B,H,Tq,hd], k/v [B,KV,Tk,hd] (same dtype, contiguous, on GPU).
 
-    Returns (out, lse). ``out_dtype`` defaults to fp32.
+    With Tq == Tk, q_offset == 0 and window == 0 this is attn_prefill_fwd; otherwise
+    attn_prefill_ex_fwd (query chunk at token q_offset, sliding window). Returns
+    (out, lse). ``out_dtype`` defaults to fp32.
     """
     import torch
 
     assert q.is_cuda and k.is_cuda and v.is_cuda, "tensors must be on the GPU"
     assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
-    B, H, T, hd = q.shape
-    KV = k.shape[1]
+    B, H, Tq, hd = q.shape
+    KV, Tk = k.shape[1], k.shape[2]
     dt = _dtype_code(q)
     odt = torch.float32 if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty(B, H, T, hd, dtype=odt, device=q.device)
+        out = torch.empty(B, H, Tq, hd, dtype=odt, device=q.device)
     if lse is None and want_lse:
-        lse = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+        lse = torch.empty(B, H, Tq, dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace, nbytes = prefill_workspace(B, T, KV, hd, dt, rope_base, q.device)
+        workspace, nbytes = prefill_workspace(B, Tk, KV, hd, dt, rope_base, q.device)
     else:
         nbytes = workspace.numel() * workspace.element_size()
-    st = attn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          lse.data_ptr() if lse is not None else None, B, T, H, KV, hd, pos0, rope_base,
-                          int(causal), alibi, dt, _dtype_code(out), workspace.data_ptr(), nbytes,
-                          _stream_ptr(stream))
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    if Tq == Tk and q_offset == 0 and window == 0:
+        st = attn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, Tq, H, KV, hd,
+                              pos0, rope_base, int(causal), alibi, dt, _dtype_code(out), workspace.data_ptr(), nbytes,
+                              _stream_ptr(stream))
+    else:
+        st = attn_prefill_ex_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, Tq, Tk, H, KV,
+                                 hd, pos0, q_offset, window, rope_base, int(causal), alibi, dt, _dtype_code(out),
+                                 workspace.data_ptr(), nbytes, _stream_ptr(stream))
     _check(st)
     return out, lse
 

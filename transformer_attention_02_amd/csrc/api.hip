@@ -111,23 +111,34 @@ size_t attn_prefill_workspace_bytes(int B, int T, int KV, int hd, int dtype, dou
   return (size_t)n * elem_bytes(dtype);
 }
 
-int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int T, int H,
-                     int KV, int hd, int pos0, double rope_base, int causal, int alibi, int dtype, int out_dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of both prefill entry points: Tq query rows that are key tokens
+// q_off .. q_off+Tq-1 of a Tk-token sequence, optional sliding window.
+int prefill_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Tq, int Tk, int H,
+                 int KV, int hd, int pos0, int q_off, int window, double rope_base, int causal, int alibi,
+                 int dtype, int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !out) return fail(ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
-  if (B <= 0 || T <= 0 || H <= 0 || KV <= 0)
-    return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d KV=%d)", B, T, H, KV);
+  if (B <= 0 || Tq <= 0 || Tk <= 0 || H <= 0 || KV <= 0)
+    return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d Tq=%d Tk=%d H=%d KV=%d)", B, Tq, Tk, H, KV);
   if (H % KV) return fail(ATTN_ERR_SHAPE, "H=%d is not a multiple of KV=%d", H, KV);
-  if (pos0 < 0 || (long long)pos0 + T > 0x7fffffffLL) return fail(ATTN_ERR_SHAPE, "pos0=%d out of range", pos0);
+  if (q_off < 0 || (long long)q_off + Tq > Tk)
+    return fail(ATTN_ERR_SHAPE, "query chunk [%d, %d) must lie inside the %d keys", q_off, q_off + Tq, Tk);
+  if (pos0 < 0 || (long long)pos0 + Tk > 0x7fffffffLL) return fail(ATTN_ERR_SHAPE, "pos0=%d out of range", pos0);
   if (H > 65535 || B > 65535 || (long long)B * KV > 65535 * 8LL)
     return fail(ATTN_ERR_SHAPE, "H, B and B*KV/8 must be <= 65535");
   if (int c = check_common(dtype, out_dtype, alibi, rope_base, hd)) return c;
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_UNSUPPORTED, "causal %d", causal);
-  if ((long long)B * H * T * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "tensor too large");
+  if (window < 0) return fail(ATTN_ERR_SHAPE, "window %d must be >= 0", window);
+  if (window > 0 && !causal) return fail(ATTN_ERR_UNSUPPORTED, "a sliding window needs causal attention");
+  if ((long long)B * H * Tq * hd > kMaxElems || (long long)B * KV * Tk * hd > kMaxElems)
+    return fail(ATTN_ERR_SHAPE, "tensor too large");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(ATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(ATTN_ERR_ALIGN, "lse must be 4-byte aligned");
-  const size_t need = attn_prefill_workspace_bytes(B, T, KV, hd, dtype, rope_base);
+  const size_t need = attn_prefill_workspace_bytes(B, Tk, KV, hd, dtype, rope_base);
   if (need) {
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
@@ -145,12 +156,16 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
   a.out = out;
   a.lse = lse;
   a.B = B;
-  a.T = T;
+  a.Tq = Tq;
+  a.Tk = Tk;
   a.H = H;
   a.KV = KV;
   a.hd = hd;
   a.group = H / KV;
   a.pos0 = pos0;
+  a.q_off = q_off;
+  // a window covering every key a query can see changes nothing
+  a.window = (window > 0 && window < q_off + Tq) ? window : 0;
   a.causal = causal;
   a.rope = rope_base != 0.0;
   a.alibi = alibi;
@@ -163,7 +178,7 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
     r.k = k;
     r.kr = workspace;
     r.heads = B * KV;
-    r.T = T;
+    r.T = Tk;
     r.hd = hd;
     r.pos0 = pos0;
     r.freqs = a.freqs;
@@ -178,6 +193,24 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, flo
     if (int c = hip_status(launch_prefill_valu(a, bf16, s), "prefill_valu launch")) return c;
   }
   return hip_status(tm.after(s), "timing event");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int T, int H,
+                     int KV, int hd, int pos0, double rope_base, int causal, int alibi, int dtype, int out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, out, lse, B, T, T, H, KV, hd, pos0, 0, 0, rope_base, causal, alibi, dtype, out_dtype,
+                      workspace, workspace_bytes, stream);
+}
+
+int attn_prefill_ex_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Tq, int Tk,
+                        int H, int KV, int hd, int pos0, int q_offset, int window, double rope_base, int causal,
+                        int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, out, lse, B, Tq, Tk, H, KV, hd, pos0, q_offset, window, rope_base, causal, alibi,
+                      dtype, out_dtype, workspace, workspace_bytes, stream);
 }
 
 namespace {

@@ -21,13 +21,15 @@ struct RopeFreqs {
 };
 
 struct PrefillArgs {
-  const void* q;     // [B,H,T,hd]
-  const void* k;     // [B,KV,T,hd] rotated keys (workspace) or raw keys when rope is off
-  const void* v;     // [B,KV,T,hd]
-  void* out;         // [B,H,T,hd]
-  float* lse;        // [B,H,T] or nullptr
-  int B, T, H, KV, hd, group;
-  int pos0;
+  const void* q;     // [B,H,Tq,hd]
+  const void* k;     // [B,KV,Tk,hd] rotated keys (workspace) or raw keys when rope is off
+  const void* v;     // [B,KV,Tk,hd]
+  void* out;         // [B,H,Tq,hd]
+  float* lse;        // [B,H,Tq] or nullptr
+  int B, Tq, Tk, H, KV, hd, group;
+  int pos0;          // position of key token 0
+  int q_off;         // query row i is key token q_off + i (q_off + Tq <= Tk)
+  int window;        // > 0: a query sees only its last `window` tokens (causal only)
   int causal;
   int rope;
   int alibi;

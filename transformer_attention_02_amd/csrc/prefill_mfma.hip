@@ -162,7 +162,7 @@ struct Dma {
 
 // One wave's online-softmax state for 32 query rows (lane n holds row qi, the
 // two half-waves split the keys of a tile), and the steps of one 64-key tile.
-template <int HD, bool ALIBI, bool CAUSAL>
+template <int HD, bool ALIBI, bool CAUSAL, bool WINDOW>
 struct WaveState {
   f32x16 oacc[HD / 32];  // O^T: lane holds query n, dims 32mb + 8(r/4) + 4hf + r%4
   bf16x8 qf[HD / 16];    // Q^T B operand, k-step s: dims 16s + 8hf .. +7
@@ -171,8 +171,9 @@ struct WaveState {
   float l_run;           // this half-wave's part of the running denominator
   float c2;              // log2(e) / sqrt(hd)
   float slope2;          // ALiBi slope * log2(e)
-  int qi;                // this lane's query row
-  int T;
+  int qi;                // this lane's query token (index in the key sequence)
+  int Tk;                // keys in the sequence
+  int window;            // sliding window in tokens (0: none)
   int lane;
   int vtr[HD / 32];      // byte offset in the V tile of this lane's V^T read, key row 8hf + (lane%16)/4
 
@@ -254,12 +255,18 @@ struct WaveState {
     // scaled, biased score in log2 units.
     float t[32];
     const int dbase = k0 + 8 * hf - qi;  // key - query at register offset 0
+    // ALiBi: register i sits at key - query = dbase + c_i with a constant c_i, so
+    // the bias costs one FMA per score when causal (slope2 * dbase is formed once;
+    // distances are exact in fp32) and an add plus a multiply otherwise.
+    const float dbf = (float)dbase;
+    const float sbase = slope2 * dbf;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const float x = i < 16 ? sa[i] : sb[i - 16];
       if constexpr (ALIBI) {
-        const float dk = (float)(dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8));
-        t[i] = fmaf(x, c2, slope2 * (CAUSAL ? dk : -fabsf(dk)));
+        const float ci = (float)(32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8));
+        const float bias = CAUSAL ? fmaf(slope2, ci, sbase) : -slope2 * fabsf(dbf + ci);
+        t[i] = fmaf(x, c2, bias);
       } else {
         t[i] = x;
       }
@@ -268,7 +275,7 @@ struct WaveState {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int dk = dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
-        const bool vis = (dk + qi < T) && (!CAUSAL || dk <= 0);
+        const bool vis = (dk + qi < Tk) && (!CAUSAL || dk <= 0) && (!WINDOW || dk > -window);
         t[i] = vis ? t[i] : -INFINITY;
       }
     }
@@ -285,10 +292,14 @@ struct WaveState {
     const bool move = ms > m_run + 8.0f;
     const float alpha = move ? __builtin_amdgcn_exp2f(m_run - ms) : 1.0f;
     m_run = move ? ms : m_run;
+    // A masked tile can hold no visible key for a row that has seen none yet
+    // (a sliding window starting inside a later tile): its weights must come
+    // out as exact zeros, not as exp2(-inf - (-inf)).
+    const float mref = (MASK && m_run == -INFINITY) ? 0.f : m_run;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      t[i] = __builtin_amdgcn_exp2f(ALIBI ? t[i] - m_run : fmaf(t[i], c2, -m_run));
+      t[i] = __builtin_amdgcn_exp2f(ALIBI ? t[i] - mref : fmaf(t[i], c2, -mref));
       ls[i % 4] += t[i];
     }
     l_run = fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
@@ -328,7 +339,7 @@ struct WaveState {
   }
 };
 
-template <int HD, bool ALIBI, bool CAUSAL, bool OUT_BF16>
+template <int HD, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using C = Cfg<HD>;
@@ -372,26 +383,32 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   const int head = kvh * a.group + hc * gm.hpw + (wave % gm.hpw);
   const int q0 = qb * gm.bm;
   const int qw0 = q0 + 32 * (wave / gm.hpw);
-  const bool wave_active = qw0 < a.T;
+  const bool wave_active = qw0 < a.Tq;
 
-  const long kvoff = ((long)b * a.KV + kvh) * (long)a.T * HD;
+  const long kvoff = ((long)b * a.KV + kvh) * (long)a.Tk * HD;
   const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k) + kvoff;
   const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v) + kvoff;
-  const int q_last = min(a.T, q0 + gm.bm) - 1;
-  const int nkt = CAUSAL ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
+  const int q_last = min(a.Tq, q0 + gm.bm) - 1;
+  // Query rows are key tokens q_off + row. Key tiles [kt_begin, nkt) hold every
+  // key some row of the workgroup sees: up to the last row's own token
+  // (causal), from the first row's window start (sliding window).
+  const int tq0 = a.q_off + q0, tq_last = a.q_off + q_last;
+  const int nkt = CAUSAL ? (tq_last / BN + 1) : (a.Tk + BN - 1) / BN;
+  const int kt_begin = WINDOW ? max(0, tq0 - a.window + 1) / BN : 0;
 
   // The first K/V tile streams into stage 0 during the Q set-up.
   Dma<HD> dma;
   dma.init(wave, lane);
-  dma.issue(Kg, Vg, 0, a.T, s0, wave);
-  // Stage 2 stands in for "tile -1": its V part is zeroed and the pending
-  // probabilities start at zero, so the first tile's deferred product adds
-  // exact zeros.
+  dma.issue(Kg, Vg, kt_begin, a.Tk, s0, wave);
+  // Stage 2 stands in for the tile before the first one: its V part is zeroed
+  // and the pending probabilities start at zero, so the first tile's deferred
+  // product adds exact zeros.
   for (int e = tid; e < C::V_BYTES / 16; e += NT) reinterpret_cast<uint4*>(s2 + C::K_BYTES)[e] = make_uint4(0, 0, 0, 0);
 
-  WaveState<HD, ALIBI, CAUSAL> ws;
-  ws.qi = qw0 + n;
-  ws.T = a.T;
+  WaveState<HD, ALIBI, CAUSAL, WINDOW> ws;
+  ws.qi = a.q_off + qw0 + n;
+  ws.Tk = a.Tk;
+  ws.window = a.window;
   ws.lane = lane;
   ws.init_offsets();
   ws.c2 = a.scale_log2;
@@ -414,7 +431,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       for (int e = tid; e < (HD / 2) * gm.bm; e += NT) {
         const int r = e % gm.bm, p = e / gm.bm;
         float c, sn;
-        rope_cos_sin(a.pos0 + q0 + r, a.freqs.rev[p], c, sn);
+        rope_cos_sin(a.pos0 + tq0 + r, a.freqs.rev[p], c, sn);
         cs[e] = make_float2(c, sn);
       }
       __syncthreads();
@@ -430,7 +447,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
           c = t.x;
           sn = t.y;
         } else {
-          rope_cos_sin(a.pos0 + qr, a.freqs.rev[p0 + p], c, sn);
+          rope_cos_sin(a.pos0 + a.q_off + qr, a.freqs.rev[p0 + p], c, sn);
         }
         const uint32_t x = comp(raw, p);
         const float x0 = bf16_bits_to_f32(x & 0xffffu), x1 = bf16_bits_to_f32(x >> 16);
@@ -438,9 +455,9 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       }
       return as_bf16x8(make_uint4(d[0], d[1], d[2], d[3]));
     };
-    const int qr = ws.qi;
+    const int qr = qw0 + n;  // query row
     const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                      (((long)b * a.H + head) * a.T + min(qr, a.T - 1)) * HD);
+                                                      (((long)b * a.H + head) * a.Tq + min(qr, a.Tq - 1)) * HD);
     uint4 raw[HD / 16];
 #pragma unroll
     for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
@@ -456,13 +473,18 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Tiles [0, kt_clean) need no mask for any row of the workgroup: every key is
-  // at or before the first query row (causal) and inside the sequence.
-  const int kt_clean = min(nkt, CAUSAL ? min((q0 + 1) / BN, a.T / BN) : a.T / BN);
+  // Tiles [kc_lo, kc_hi) need no mask for any row of the workgroup: every key
+  // is at or before the first row's token (causal), inside the last row's
+  // window and inside the sequence.
+  const int kc_lo = WINDOW ? max(kt_begin, (max(0, tq_last - a.window + 1) + BN - 1) / BN) : kt_begin;
+  const int kc_hi = min(nkt, CAUSAL ? min((tq0 + 1) / BN, a.Tk / BN) : a.Tk / BN);
   // Per tile: start the DMA of tile kt+1, the scores of tile kt, then its
   // softmax under the deferred V^T product of tile kt-1; the wait + barrier at
   // the end publishes tile kt+1 and retires stage kt-1.
-  bool pending = true;  // pprev still owes its V^T product
+  // pprev owes its V^T product. Without a window every active wave runs the
+  // first tile, so this starts true (the zero operands of "tile -1" are
+  // harmless); with a window a wave may skip the first tiles and starts false.
+  bool pending = !WINDOW;
   auto step = [&](int kt, auto mask_tag, auto phase_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(phase_tag)::value;
@@ -470,9 +492,12 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     unsigned char* prv = P == 0 ? s2 : (P == 1 ? s0 : s1);
     unsigned char* nxt = P == 0 ? s1 : (P == 1 ? s2 : s0);
     const int k0 = kt * BN;
-    if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.T, nxt, wave);
-    // in a masked tile a wave may be past its last visible key
-    const bool run = wave_active && !(MASK && CAUSAL && k0 > qw0 + 31);
+    if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.Tk, nxt, wave);
+    // in a masked tile a wave may be past its last visible key (causal) or
+    // before its first one (sliding window)
+    const int tw0 = a.q_off + qw0;
+    const bool run = wave_active && !(MASK && ((CAUSAL && k0 > tw0 + 31) ||
+                                               (WINDOW && k0 + BN - 1 < tw0 - a.window + 1)));
     if (run) {
       f32x16 sa, sb;
       ws.scores((LdsBytes)cur, sa, sb);
@@ -481,7 +506,10 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       __builtin_amdgcn_s_setprio(1);
       ws.template softmax_pv<MASK>(sa, sb, k0, (LdsBytes)(prv + C::K_BYTES));
       __builtin_amdgcn_s_setprio(0);
-    } else if (MASK && wave_active && pending) {
+      if constexpr (MASK && WINDOW) pending = true;
+    } else if (MASK && pending) {
+      // past the wave's last visible key: settle the owed product (the wave
+      // does not run again)
       ws.pv((LdsBytes)(prv + C::K_BYTES), ws.pprev);
       pending = false;
     }
@@ -493,35 +521,46 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
-  // Clean tiles in whole rounds of the 3-stage ring; the masked phase (plus at
-  // most two clean tiles) then starts again at stage 0.
-  const int kt3 = kt_clean - kt_clean % 3;
-  int kt = 0;
-  for (; kt < kt3; kt += 3) {
+  // Tile kt uses ring stage (kt - kt_begin) % 3, and every loop below starts a
+  // round of the ring at stage 0, so each step names its stages statically.
+  // Masked rounds run the masked step, which is also correct for clean tiles.
+  int kt = kt_begin;
+  auto masked_rounds = [&](int end) __attribute__((always_inline)) {
+    while (kt < end) {
+      step(kt, M{}, P0{});
+      if (++kt >= end) break;
+      step(kt, M{}, P1{});
+      if (++kt >= end) break;
+      step(kt, M{}, P2{});
+      ++kt;
+    }
+  };
+  if constexpr (WINDOW) {
+    // tiles at the window's start, up to the first round boundary at or after
+    // the first clean tile
+    masked_rounds(min(nkt, kt_begin + (kc_lo - kt_begin + 2) / 3 * 3));
+  }
+  if constexpr (WINDOW) {
+    if (kt + 3 <= kc_hi) pending = true;  // every active wave runs a clean tile
+  }
+  for (; kt + 3 <= kc_hi; kt += 3) {
     step(kt, F{}, P0{});
     step(kt + 1, F{}, P1{});
     step(kt + 2, F{}, P2{});
   }
-  while (kt < nkt) {
-    step(kt, M{}, P0{});
-    if (++kt >= nkt) break;
-    step(kt, M{}, P1{});
-    if (++kt >= nkt) break;
-    step(kt, M{}, P2{});
-    ++kt;
-  }
+  masked_rounds(nkt);
   if (!wave_active) return;
   // the last tile's V^T product (no DMA is in flight any more)
   if (pending) {
-    const int p = (nkt - 1) % 3;
+    const int p = (nkt - 1 - kt_begin) % 3;
     ws.pv((LdsBytes)((p == 0 ? s0 : (p == 1 ? s1 : s2)) + C::K_BYTES), ws.pprev);
   }
 
   const float l_tot = ws.l_run + xhalf(ws.l_run);
-  const int qi = ws.qi;
-  if (qi >= a.T) return;
+  const int qi = qw0 + n;  // query row
+  if (qi >= a.Tq) return;
   const float inv_l = 1.0f / l_tot;
-  const long orow = (((long)b * a.H + head) * a.T + qi) * HD;
+  const long orow = (((long)b * a.H + head) * a.Tq + qi) * HD;
 #pragma unroll
   for (int mb = 0; mb < HD / 32; ++mb) {
 #pragma unroll
@@ -537,7 +576,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       }
     }
   }
-  if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.T + qi] = (ws.m_run + log2f(l_tot)) * 0.69314718055994531f;
+  if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.Tq + qi] = (ws.m_run + log2f(l_tot)) * 0.69314718055994531f;
 }
 
 GridMap make_grid(const PrefillArgs& a) {
@@ -545,29 +584,33 @@ GridMap make_grid(const PrefillArgs& a) {
   gm.hpw = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
   gm.hchunks = a.group / gm.hpw;
   gm.bm = 32 * (NW / gm.hpw);
-  gm.nqb = (a.T + gm.bm - 1) / gm.bm;
+  gm.nqb = (a.Tq + gm.bm - 1) / gm.bm;
   gm.units = a.B * a.KV * gm.hchunks;
   gm.xcd_aware = (gm.units % 8) == 0;
   return gm;
 }
 
-template <int HD, bool ALIBI, bool CAUSAL>
+template <int HD, bool ALIBI, bool CAUSAL, bool WINDOW>
 void launch_out(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
   if (a.out_bf16) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, true>), grid, dim3(NT), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, true, WINDOW>), grid, dim3(NT), 0, s, a, gm);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, false>), grid, dim3(NT), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, false, WINDOW>), grid, dim3(NT), 0, s, a, gm);
   }
 }
 
+// The sliding window is a separate instance (causal only), so the plain
+// kernels carry none of its masking or tile-skipping code.
 template <int HD>
 void launch_hd(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
   if (a.alibi) {
-    if (a.causal) launch_out<HD, true, true>(a, gm, grid, s);
-    else launch_out<HD, true, false>(a, gm, grid, s);
+    if (a.window > 0) launch_out<HD, true, true, true>(a, gm, grid, s);
+    else if (a.causal) launch_out<HD, true, true, false>(a, gm, grid, s);
+    else launch_out<HD, true, false, false>(a, gm, grid, s);
   } else {
-    if (a.causal) launch_out<HD, false, true>(a, gm, grid, s);
-    else launch_out<HD, false, false>(a, gm, grid, s);
+    if (a.window > 0) launch_out<HD, false, true, true>(a, gm, grid, s);
+    else if (a.causal) launch_out<HD, false, true, false>(a, gm, grid, s);
+    else launch_out<HD, false, false, false>(a, gm, grid, s);
   }
 }
 
@@ -575,7 +618,7 @@ void launch_hd(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s
 
 bool prefill_mfma_supported(const PrefillArgs& a, int bf16) {
   if (!bf16 || (a.hd != 64 && a.hd != 128)) return false;
-  if ((long)a.T * a.hd * 2 >= (1L << 31)) return false;  // buffer descriptors hold 32-bit sizes
+  if ((long)a.Tk * a.hd * 2 >= (1L << 31)) return false;  // buffer descriptors hold 32-bit sizes
   const GridMap gm = make_grid(a);
   return (long)gm.units * gm.nqb < (1L << 31);
 }

@@ -83,9 +83,10 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
   const int g = h / a.group;
   const int t = threadIdx.x;
   const int i = qb * BQ + t;
-  const bool active = i < a.T;
-  const long qrow = (((long)b * a.H + h) * a.T + (active ? i : 0)) * HD;
-  const long kvbase = ((long)b * a.KV + g) * (long)a.T * HD;
+  const bool active = i < a.Tq;
+  const int ti = a.q_off + i;  // this query's token index in the key sequence
+  const long qrow = (((long)b * a.H + h) * a.Tq + (active ? i : 0)) * HD;
+  const long kvbase = ((long)b * a.KV + g) * (long)a.Tk * HD;
 
   float q[HD], acc[HD];
 #pragma unroll
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
     float y0 = x0, y1 = x1;
     if (a.rope) {
       float c, s;
-      rope_cos_sin(a.pos0 + i, a.freqs.rev[p], c, s);
+      rope_cos_sin(a.pos0 + ti, a.freqs.rev[p], c, s);
       y0 = rot0(x0, x1, c, s);
       y1 = rot1(x0, x1, c, s);
     }
@@ -106,14 +107,18 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
   const float slope2 = a.alibi ? alibi_slope(a.alibi, h, a.H) * 1.4426950408889634f : 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int ntiles_all = (a.T + BK - 1) / BK;
-  const int ntiles = a.causal ? min(qb + 1, ntiles_all) : ntiles_all;
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // key tiles the block's rows can see: up to the last row's token (causal),
+  // from the first row's window start (sliding window)
+  const int ntiles_all = (a.Tk + BK - 1) / BK;
+  const int t_last = a.q_off + min(a.Tq, qb * BQ + BQ) - 1;
+  const int ntiles = a.causal ? min(t_last / BK + 1, ntiles_all) : ntiles_all;
+  const int kt0 = a.window ? max(0, a.q_off + qb * BQ - a.window + 1) / BK : 0;
+  for (int kt = kt0; kt < ntiles; ++kt) {
     __syncthreads();
     for (int e = t; e < BK * HD; e += 64) {
       const int r = e / HD, d = e - r * HD;
       const int key = kt * BK + r;
-      const bool in = key < a.T;
+      const bool in = key < a.Tk;
       ks[r][d] = in ? ld<BF16>(a.k, kvbase + (long)key * HD + d) : 0.f;
       vs[r][d] = in ? ld<BF16>(a.v, kvbase + (long)key * HD + d) : 0.f;
     }
@@ -128,8 +133,8 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
         float dot = 0.f;
 #pragma unroll
         for (int d = 0; d < HD; ++d) dot = fmaf(q[d], ks[j0 + jj][d], dot);
-        const int dist = i - key;
-        const bool vis = key < a.T && (!a.causal || dist >= 0);
+        const int dist = ti - key;
+        const bool vis = key < a.Tk && (!a.causal || dist >= 0) && (!a.window || dist < a.window);
         const float x = dot - slope2 * (float)(dist < 0 ? -dist : dist);
         sc[jj] = vis ? x : -INFINITY;
         mt = fmaxf(mt, sc[jj]);
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
   }
   if (!active) return;
   const float inv_l = 1.0f / l;
-  const long orow = (((long)b * a.H + h) * a.T + i) * HD;
+  const long orow = (((long)b * a.H + h) * a.Tq + i) * HD;
   if (a.out_bf16) {
     uint32_t* o = reinterpret_cast<uint32_t*>(a.out) + (orow >> 1);
 #pragma unroll
@@ -162,12 +167,12 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
 #pragma unroll
     for (int d = 0; d < HD; ++d) o[d] = acc[d] * inv_l;
   }
-  if (a.lse) a.lse[((long)b * a.H + h) * a.T + i] = (m + log2f(l)) * 0.69314718055994531f;
+  if (a.lse) a.lse[((long)b * a.H + h) * a.Tq + i] = (m + log2f(l)) * 0.69314718055994531f;
 }
 
 template <int BF16>
 hipError_t launch_valu_hd(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid((a.T + 63) / 64, a.H, a.B);
+  dim3 grid((a.Tq + 63) / 64, a.H, a.B);
   switch (a.hd) {
     case 8: hipLaunchKernelGGL((prefill_valu_kernel<BF16, 8>), grid, dim3(64), 0, s, a); break;
     case 16: hipLaunchKernelGGL((prefill_valu_kernel<BF16, 16>), grid, dim3(64), 0, s, a); break;
