@@ -16,7 +16,8 @@ kernel on its own stream; ``decode.roofline`` is the same for the split-KV
 kernel. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
 same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|prefill|decode|alibi|small|copy]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload all|prefill|decode|alibi|small|window|chunk|copy]
                        [--no-cpu-baseline] [--no-ceilings]
 """
 from __future__ import annotations
@@ -108,8 +109,8 @@ class Prefill:
         self.w, self.bd = w, bd
         q, k, v = W.prefill_inputs(w)
         self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
-        self.out = torch.empty(w.B, w.H, w.T, w.hd, dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty(w.B, w.H, w.T, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.B, w.H, w.rows, w.hd, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(w.B, w.H, w.rows, dtype=torch.float32, device=dev)
         dt = bd.ATTN_DTYPE_BF16 if w.dtype == "bf16" else bd.ATTN_DTYPE_F32
         self.dt = dt
         self.ws, self.ws_bytes = bd.prefill_workspace(w.B, w.T, w.KV, w.hd, dt, w.rope_base, dev)
@@ -118,10 +119,16 @@ class Prefill:
         w, bd = self.w, self.bd
         if events:
             bd.attn_set_timing_events(*events)
-        st = bd.attn_prefill_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
-                                 self.lse.data_ptr(), w.B, w.T, w.H, w.KV, w.hd, w.pos0, w.rope_base,
-                                 int(w.causal), w.alibi, self.dt, bd.ATTN_DTYPE_BF16, self.ws.data_ptr(),
-                                 self.ws_bytes, stream)
+        if w.Tq or w.q_offset or w.window:
+            st = bd.attn_prefill_ex_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
+                                        self.lse.data_ptr(), w.B, w.rows, w.T, w.H, w.KV, w.hd, w.pos0, w.q_offset,
+                                        w.window, w.rope_base, int(w.causal), w.alibi, self.dt, bd.ATTN_DTYPE_BF16,
+                                        self.ws.data_ptr(), self.ws_bytes, stream)
+        else:
+            st = bd.attn_prefill_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
+                                     self.lse.data_ptr(), w.B, w.T, w.H, w.KV, w.hd, w.pos0, w.rope_base,
+                                     int(w.causal), w.alibi, self.dt, bd.ATTN_DTYPE_BF16, self.ws.data_ptr(),
+                                     self.ws_bytes, stream)
         if st != bd.ATTN_OK:
             raise RuntimeError(f"attn_prefill_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
 
@@ -174,12 +181,13 @@ def cpu_baseline_leg(pre, dec, heads, seqs):
         heads = max(g, heads // g * g)
         qs, ks, vs = f64(pre.q[0:1, :heads]), f64(pre.k[0:1, :heads // g]), f64(pre.v[0:1, :heads // g])
         t0 = time.perf_counter()
-        ref, _ = attention_prefill(qs, ks, vs, pos0=w.pos0, rope_base=w.rope_base, causal=w.causal, alibi=w.alibi)
+        ref, _ = attention_prefill(qs, ks, vs, pos0=w.pos0, rope_base=w.rope_base, causal=w.causal, alibi=w.alibi,
+                                   q_offset=w.q_offset, window=w.window)
         dt = time.perf_counter() - t0
-        flops = 4.0 * heads * w.hd * (w.T * (w.T + 1) / 2 if w.causal else w.T * w.T)
+        flops = 4.0 * heads * w.hd * w.pairs()
         err = float(np.abs(f64(pre.out[0:1, :heads]) - ref).max())
         res.update(value=flops / dt / 1e12, unit="TFLOP/s", seconds=dt,
-                   sample=f"{heads} query heads of batch 0 ({heads // g} KV heads), all {w.T} causal rows: "
+                   sample=f"{heads} query heads of batch 0 ({heads // g} KV heads), all {w.rows} query rows: "
                           f"{flops / w.flops() * 100:.2f}% of the prefill step",
                    max_abs_err_vs_gpu_bf16_out=err)
     if dec is not None:
@@ -211,7 +219,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="all", choices=["all", "prefill", "decode", "alibi", "small", "copy"],
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "prefill", "decode", "alibi", "small", "window", "chunk", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -255,7 +264,8 @@ def main():
                           "ms": ms, "GB/s": nbytes / ms / 1e6}), flush=True)
         return
 
-    pre_w = {"all": W.LLAMA3_8B, "prefill": W.LLAMA3_8B, "alibi": W.ALIBI_MHA, "small": W.SMALL_BF16}.get(args.workload)
+    pre_w = {"all": W.LLAMA3_8B, "prefill": W.LLAMA3_8B, "alibi": W.ALIBI_MHA, "small": W.SMALL_BF16,
+             "window": W.LLAMA3_WINDOW, "chunk": W.LLAMA3_CHUNK}.get(args.workload)
     pre = Prefill(pre_w, dev, bd, W, torch) if pre_w is not None else None
     dec = Decode(W.KV_DECODE, dev, bd, W, torch) if args.workload in ("all", "decode") else None
     log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None}")
@@ -307,6 +317,8 @@ def main():
         cfg["prefill"] = {"B": w.B, "T": w.T, "H": w.H, "KV": w.KV, "hd": w.hd, "rope_base": w.rope_base,
                           "causal": w.causal, "alibi": w.alibi, "out_dtype": "bf16", "flops": w.flops(),
                           "call_ms": pc, "kernel_ms": pk}
+        if w.Tq or w.q_offset or w.window:
+            cfg["prefill"].update(query_rows=w.rows, q_offset=w.q_offset, window=w.window)
         cfg["prefill"]["kernel_ms_median"], cfg["prefill"]["kernel_ms_min"] = med_min("pk")
         traffic = traffic_for("prefill_mfma_kernel", PREFILL_SOURCES, w.name)
         line["roofline"] = {"bound": "mfma", "achieved": kt, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

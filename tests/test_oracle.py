@@ -483,6 +483,21 @@ def test_prefill_flop_count():
     assert W.LLAMA3_8B.flops() == pytest.approx(5.4992e11, rel=1e-4)
 
 
+@pytest.mark.parametrize("T,Tq,q_offset,window", [(9, 0, 0, 0), (9, 0, 0, 3), (12, 5, 7, 0), (12, 5, 7, 4),
+                                                  (12, 3, 2, 100), (30, 30, 0, 1)])
+def test_workload_pair_counts(T, Tq, q_offset, window):
+    """The benchmark's visible-pair count equals a count over the oracle's own mask."""
+    w = W.PrefillWorkload("t", 1, T, 2, 1, 8, W.BF16, 0, 0.0, Tq=Tq, q_offset=q_offset, window=window)
+    rows = Tq or T
+    # a V of one-hot key indicators makes the oracle's output count the visible keys with Q = 0
+    q = np.zeros((1, 2, rows, T))
+    k = np.zeros((1, 1, T, T))
+    v = np.eye(T)[None, None]
+    out, _ = attention_prefill(q, k, v, rope_base=0.0, q_offset=q_offset, window=window)
+    visible = int(round((out[0, 0] > 0).sum()))
+    assert w.pairs() == visible
+
+
 def test_decode_workload_lengths():
     lens = W.KV_DECODE.lengths()
     assert len(lens) == 64 and lens.min() >= 512 and lens.max() <= 8192

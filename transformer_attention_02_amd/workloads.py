@@ -42,11 +42,27 @@ class PrefillWorkload:
     pos0: int = 0
     causal: bool = True
     alibi: int = 0  # 0 none, 1 geometric 2^(-8(h+1)/H), 2 page-1 heuristic 2^(-2(h+1)/H)
+    Tq: int = 0        # query rows (a chunk of the T tokens); 0 means all T
+    q_offset: int = 0  # token index of the first query row
+    window: int = 0    # sliding window in tokens (causal only); 0 means none
+
+    @property
+    def rows(self) -> int:
+        return self.Tq or self.T
+
+    def pairs(self) -> int:
+        """Visible (query, key) pairs per head: causal keys up to the query's own
+        token, within the window if any; all T keys when not causal."""
+        if not self.causal:
+            return self.rows * self.T
+        if not self.window:
+            a, b = self.q_offset + 1, self.q_offset + self.rows   # sum of (t + 1) over the chunk
+            return (a + b) * self.rows // 2
+        return sum(min(t + 1, self.window) for t in range(self.q_offset, self.q_offset + self.rows))
 
     def flops(self) -> float:
         """Algorithmic flops: two contractions over the visible (query, key) pairs."""
-        pairs = self.T * (self.T + 1) // 2 if self.causal else self.T * self.T
-        return 4.0 * self.B * self.H * self.hd * pairs
+        return 4.0 * self.B * self.H * self.hd * self.pairs()
 
     def io_bytes(self, out_elem: int = 4) -> int:
         e = 4 if self.dtype == F32 else 2
@@ -88,10 +104,17 @@ LLAMA3_8B = PrefillWorkload("llama3-8b-prefill B=4 T=4096 H=32 KV=8 hd=128 rope=
                             4, 4096, 32, 8, 128, BF16, 3, 500000.0)
 ALIBI_MHA = PrefillWorkload("alibi-mha-prefill B=8 T=2048 H=16 KV=16 hd=128",
                             8, 2048, 16, 16, 128, BF16, 4, 0.0, alibi=1)
+# the Llama-3-8B prompt with a 1024-token sliding window, and its last 512
+# tokens processed as one chunk against the whole prompt's keys (same inputs)
+LLAMA3_WINDOW = PrefillWorkload("llama3-8b-prefill sliding window W=1024 B=4 T=4096 H=32 KV=8 hd=128 rope=5e5",
+                                4, 4096, 32, 8, 128, BF16, 3, 500000.0, window=1024)
+LLAMA3_CHUNK = PrefillWorkload("llama3-8b chunked prefill: tokens 3584..4095 over 4096 keys, B=4 H=32 KV=8 hd=128",
+                               4, 4096, 32, 8, 128, BF16, 3, 500000.0, Tq=512, q_offset=3584)
 KV_DECODE = DecodeWorkload("kv-decode B=64 len~U[512,8192] H=32 KV=8 hd=128",
                            64, 32, 8, 128, 512, 8192, 5, 5, 10000.0)
 
-PREFILL_WORKLOADS = {"tiny": TINY_FP32, "small": SMALL_BF16, "llama3": LLAMA3_8B, "alibi": ALIBI_MHA}
+PREFILL_WORKLOADS = {"tiny": TINY_FP32, "small": SMALL_BF16, "llama3": LLAMA3_8B, "alibi": ALIBI_MHA,
+                     "window": LLAMA3_WINDOW, "chunk": LLAMA3_CHUNK}
 
 
 def lab_instance():
@@ -150,6 +173,8 @@ def prefill_inputs(w: PrefillWorkload, *, B: int | None = None, T: int | None = 
     q = draw(g, (B, w.H, T, w.hd))
     k = draw(g, (B, w.KV, T, w.hd))
     v = draw(g, (B, w.KV, T, w.hd))
+    if w.Tq:  # a chunk: the query rows of those tokens, drawn with the whole prompt
+        q = q[:, :, w.q_offset:w.q_offset + w.Tq].contiguous()
     return q, k, v
 
 
