@@ -7,6 +7,7 @@ from .attention import (  # noqa: F401
     apply_rope,
     attention_decode,
     attention_prefill,
+    attention_prefill_bwd,
     kv_bytes_per_token,
     prefill_flops,
     rope_inv_freq,

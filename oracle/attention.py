@@ -236,6 +236,61 @@ def attention_decode(q, k_new, v_new, k_cache, v_cache, cache_lens, *, rope_base
     return out, lse, k_slot, v_slot
 
 
+def attention_prefill_bwd(q, k, v, dout, *, pos0: int = 0, rope_base: float = 10000.0, causal: bool = True,
+                          alibi: int = ALIBI_NONE):
+    """Gradients of sum(out * dout) with respect to the pre-rotation q, k and v.
+
+    The backward of the same definition (the gradient-flow checks of the
+    multi-head and pure-Python pages, and the pure-Python page's finite-difference
+    test, exercise exactly these derivatives). With the rotated q', k' and the
+    softmax weights p_ij of each visible pair:
+      dv_j  = sum_i p_ij dout_i                       (summed over the group's heads)
+      dp_ij = <dout_i, v_j>
+      ds_ij = p_ij (dp_ij - sum_l p_il dp_il)         (softmax derivative)
+      dq'_i = scale sum_j ds_ij k'_j,   dk'_j = scale sum_i ds_ij q'_i
+    and the rotation is orthogonal, so dq = R(p_i)^T dq' = R(-p_i) dq' (same for
+    k). The ALiBi bias does not depend on q, k or v. q, k, v, dout as for
+    attention_prefill (Tq = Tk = T); returns (dq [B,H,T,hd], dk [B,KV,T,hd],
+    dv [B,KV,T,hd]) in fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, T, hd = q.shape
+    KV = k.shape[1]
+    if H % KV:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    group = H // KV
+    scale = 1.0 / math.sqrt(hd)
+    slopes = alibi_slopes(H, alibi)
+    positions = pos0 + np.arange(T)
+    idx = np.arange(T)
+    vis = (idx[None, :] <= idx[:, None]) if causal else np.ones((T, T), dtype=bool)
+    dist = np.abs(idx[:, None] - idx[None, :]).astype(np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for g in range(KV):
+            kr = apply_rope(k[b, g], positions, rope_base)
+            dkr = np.zeros((T, hd))
+            for h in range(g * group, (g + 1) * group):
+                qr = apply_rope(q[b, h], positions, rope_base)
+                s = (qr @ kr.T) * scale - slopes[h] * dist
+                s = np.where(vis, s, -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                do = dout[b, h]
+                dv[b, g] += p.T @ do
+                dp = do @ v[b, g].T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h] = apply_rope(ds @ kr * scale, -positions, rope_base)
+                dkr += ds.T @ qr * scale
+            dk[b, g] = apply_rope(dkr, -positions, rope_base)
+    return dq, dk, dv
+
+
 def prefill_flops(B: int, H: int, T: int, hd: int, causal: bool = True) -> float:
     """Algorithmic flops of the forward: 2 contractions x 2 flops per visible (i, j) pair per dim."""
     pairs = T * (T + 1) / 2 if causal else T * T

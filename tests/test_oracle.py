@@ -29,6 +29,7 @@ from oracle import (
     apply_rope,
     attention_decode,
     attention_prefill,
+    attention_prefill_bwd,
     kv_bytes_per_token,
     prefill_flops,
 )
@@ -186,6 +187,96 @@ def test_chunk_and_window_match_torch_sdpa(window, q_offset):
     out, _ = attention_prefill(q.numpy(), k.numpy(), v.numpy(), pos0=pos0, rope_base=base, causal=True,
                                q_offset=q_offset, window=window)
     assert np.abs(out - ref.numpy()).max() < 1e-12
+
+
+# ------------------------------------------------------------------- backward
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("alibi", [ALIBI_NONE, ALIBI_GEOMETRIC])
+@pytest.mark.parametrize("base", [0.0, 10000.0])
+def test_backward_matches_torch_autograd(causal, alibi, base):
+    """Gradients of sum(out * dout) against torch autograd through its own softmax
+    attention routine (fp64), RoPE by torch's complex form, ALiBi as a float mask."""
+    g = torch.Generator().manual_seed(13)
+    B, H, KV, T, hd = 2, 6, 2, 21, 8
+    q = torch.randn(B, H, T, hd, generator=g, dtype=torch.float64, requires_grad=True)
+    k = torch.randn(B, KV, T, hd, generator=g, dtype=torch.float64, requires_grad=True)
+    v = torch.randn(B, KV, T, hd, generator=g, dtype=torch.float64, requires_grad=True)
+    dout = torch.randn(B, H, T, hd, generator=g, dtype=torch.float64)
+    pos0 = 4
+    qr, kr = (torch_rope(q, pos0, base), torch_rope(k, pos0, base)) if base else (q, k)
+    mask = None
+    if alibi:
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float64)
+        i = torch.arange(T, dtype=torch.float64)
+        mask = -slopes[:, None, None] * (i[:, None] - i[None, :]).abs()
+        if causal:
+            mask = mask.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+    out = F.scaled_dot_product_attention(qr, kr, v, attn_mask=mask, is_causal=causal and mask is None,
+                                         enable_gqa=True)
+    (out * dout).sum().backward()
+    dq, dk, dv = attention_prefill_bwd(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(), dout.numpy(),
+                                       pos0=pos0, rope_base=base, causal=causal, alibi=alibi)
+    assert np.abs(dq - q.grad.numpy()).max() < 1e-12
+    assert np.abs(dk - k.grad.numpy()).max() < 1e-12
+    assert np.abs(dv - v.grad.numpy()).max() < 1e-12
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of the forward definition (the pure-Python page checks its
+    gradients the same way), every input element of a tiny case."""
+    rng = np.random.default_rng(14)
+    B, H, KV, T, hd = 1, 2, 1, 4, 4
+    q = rng.normal(size=(B, H, T, hd))
+    k = rng.normal(size=(B, KV, T, hd))
+    v = rng.normal(size=(B, KV, T, hd))
+    dout = rng.normal(size=(B, H, T, hd))
+    kw = dict(pos0=3, rope_base=10000.0, causal=True, alibi=ALIBI_GEOMETRIC)
+    dq, dk, dv = attention_prefill_bwd(q, k, v, dout, **kw)
+
+    def loss(q_, k_, v_):
+        return float((attention_prefill(q_, k_, v_, **kw)[0] * dout).sum())
+
+    eps = 1e-6
+    for x, grad in ((q, dq), (k, dk), (v, dv)):
+        for ix in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[ix] += eps
+            xm[ix] -= eps
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(num - grad[ix]) < 1e-7, (ix, num, grad[ix])
+
+
+def test_backward_closed_form_zero_query():
+    """Q = 0 makes every visible weight 1/(i+1), so dv_j = sum_{i>=j} dout_i / (i+1)."""
+    rng = np.random.default_rng(15)
+    B, H, KV, T, hd = 1, 3, 1, 9, 6
+    q = np.zeros((B, H, T, hd))
+    k = rng.normal(size=(B, KV, T, hd))
+    v = rng.normal(size=(B, KV, T, hd))
+    dout = rng.normal(size=(B, H, T, hd))
+    _, _, dv = attention_prefill_bwd(q, k, v, dout, rope_base=10000.0)
+    ref = np.zeros((T, hd))
+    for j in range(T):
+        for i in range(j, T):
+            ref[j] += dout[0, :, i].sum(axis=0) / (i + 1)
+    assert np.abs(dv[0, 0] - ref).max() < 1e-13
+
+
+def test_backward_gqa_sums_the_group():
+    """A KV head's gradient is the sum of the gradients of the repeated-KV MHA heads."""
+    rng = np.random.default_rng(16)
+    B, H, KV, T, hd = 2, 4, 2, 7, 4
+    q = rng.normal(size=(B, H, T, hd))
+    k = rng.normal(size=(B, KV, T, hd))
+    v = rng.normal(size=(B, KV, T, hd))
+    dout = rng.normal(size=(B, H, T, hd))
+    dq, dk, dv = attention_prefill_bwd(q, k, v, dout)
+    dq2, dk2, dv2 = attention_prefill_bwd(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), dout)
+    assert np.abs(dq - dq2).max() < 1e-13
+    assert np.abs(dk - dk2.reshape(B, KV, 2, T, hd).sum(axis=2)).max() < 1e-13
+    assert np.abs(dv - dv2.reshape(B, KV, 2, T, hd).sum(axis=2)).max() < 1e-13
 
 
 # ---------------------------------------------------- the lab page's properties
