@@ -152,6 +152,41 @@ int attn_prefill_ex_fwd(const void* q, const void* k, const void* v, void* out, 
                         int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace attn_prefill_bwd needs: rotated copies of K and Q
+ * (only when rope_base != 0) and one fp32 per query row. 0 for invalid sizes.
+ */
+size_t attn_prefill_bwd_workspace_bytes(int B, int T, int H, int KV, int hd, int dtype, double rope_base);
+
+/*
+ * Backward of attn_prefill_fwd: the gradients of sum(out * dout) with respect
+ * to the pre-rotation q, k and v (the derivative of the softmax attention of
+ * "Building Grouped-Query Attention with RoPE and Flash Attention from
+ * Scratch", Step 3, whose backward the multi-head page's gradient-flow test and
+ * the pure-Python page's finite-difference test exercise). The attention
+ * weights are recomputed from q, k and the forward's lse (never stored):
+ *   dv_j = sum_i p_ij dout_i,  ds_ij = p_ij (<dout_i, v_j> - <dout_i, out_i>),
+ *   dq = R(-pos) scale sum_j ds_ij k'_j,  dk = R(-pos) scale sum_i ds_ij q'_i,
+ * with k', q' rotated; GQA sums dk, dv over the group's query heads.
+ *
+ *   q, k, v    as for attn_prefill_fwd (dtype, pre-rotation)
+ *   out        [B, H, T, hd]  the forward's output (out_dtype)
+ *   lse        [B, H, T]      the forward's fp32 log-sum-exp (required)
+ *   dout       [B, H, T, hd]  gradient of the loss w.r.t. out (out_dtype)
+ *   dq         [B, H, T, hd]  grad_dtype (written)
+ *   dk, dv     [B, KV, T, hd] grad_dtype (written, not accumulated)
+ *   pos0, rope_base, causal, alibi as in the forward call.
+ *   workspace: at least attn_prefill_bwd_workspace_bytes(...) bytes.
+ *
+ * Same validation rules and codes as attn_prefill_fwd; grad_dtype in {F32,
+ * BF16}. bf16 inputs with hd in {64,128} run on matrix-core kernels; every
+ * other supported case on vector-ALU kernels with fp32 arithmetic.
+ */
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int T, int H, int KV, int hd,
+                     int pos0, double rope_base, int causal, int alibi, int dtype, int out_dtype,
+                     int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace attn_decode_fwd needs for its split-KV partials
  * (fp32 partial outputs and their max / denominator per split). 0 for invalid
  * sizes.

@@ -110,6 +110,43 @@ def test_prefill_ex_validation(kw, code):
     assert bd.attn_last_error() != ""
 
 
+def _bwd(**kw):
+    args = dict(q=FAKE, k=FAKE2, v=FAKE3, out=FAKE4, lse=0x50000, dout=0x60000, dq=0x70000, dk=0x80000, dv=0x90000,
+                B=1, T=16, H=4, KV=2, hd=64, pos0=0, rope_base=10000.0, causal=1, alibi=0,
+                dtype=bd.ATTN_DTYPE_BF16, out_dtype=bd.ATTN_DTYPE_BF16, grad_dtype=bd.ATTN_DTYPE_F32,
+                workspace=0x100000, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return bd.attn_prefill_bwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), bd.ATTN_ERR_NULL),
+    (dict(dout=None), bd.ATTN_ERR_NULL),
+    (dict(dk=None), bd.ATTN_ERR_NULL),
+    (dict(T=0), bd.ATTN_ERR_SHAPE),
+    (dict(H=6, KV=4), bd.ATTN_ERR_SHAPE),
+    (dict(hd=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(grad_dtype=5), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(dq=0x70004), bd.ATTN_ERR_ALIGN),
+    (dict(lse=0x50002), bd.ATTN_ERR_ALIGN),
+    (dict(workspace=None), bd.ATTN_ERR_WORKSPACE),
+    (dict(workspace_bytes=4096), bd.ATTN_ERR_WORKSPACE),
+])
+def test_backward_validation(kw, code):
+    st = _bwd(**kw)
+    assert st == code, (st, bd.attn_last_error())
+    assert bd.attn_last_error() != ""
+
+
+def test_backward_workspace_sizes():
+    n = bd.attn_prefill_bwd_workspace_bytes(4, 4096, 32, 8, 128, bd.ATTN_DTYPE_BF16, 500000.0)
+    assert n >= (4 * 8 + 4 * 32) * 4096 * 128 * 2 + 4 * 32 * 4096 * 4 and n % 256 == 0
+    n0 = bd.attn_prefill_bwd_workspace_bytes(4, 4096, 32, 8, 128, bd.ATTN_DTYPE_BF16, 0.0)
+    assert n0 == 4 * 32 * 4096 * 4   # no rotated copies without RoPE
+    assert bd.attn_prefill_bwd_workspace_bytes(0, 1, 1, 1, 8, bd.ATTN_DTYPE_F32, 1e4) == 0
+
+
 def test_prefill_workspace_sizes():
     assert bd.attn_prefill_workspace_bytes(4, 4096, 8, 128, bd.ATTN_DTYPE_BF16, 500000.0) == 4 * 8 * 4096 * 128 * 2
     assert bd.attn_prefill_workspace_bytes(1, 6, 2, 8, bd.ATTN_DTYPE_F32, 10000.0) == 6 * 2 * 8 * 4

@@ -40,6 +40,8 @@ EXPORTS = (
     "attn_prefill_workspace_bytes",
     "attn_prefill_fwd",
     "attn_prefill_ex_fwd",
+    "attn_prefill_bwd_workspace_bytes",
+    "attn_prefill_bwd",
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
 )
@@ -58,6 +60,9 @@ _SIGS = {
     "attn_prefill_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I, _I, _I, _P, _S, _P]),
     "attn_prefill_ex_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _D, _I, _I, _I, _I, _P, _S,
                                  _P]),
+    "attn_prefill_bwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _D]),
+    "attn_prefill_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I, _I, _I, _I, _P,
+                              _S, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I, _P, _S, _P]),
 }
@@ -123,6 +128,16 @@ def attn_prefill_ex_fwd(q, k, v, out, lse, B, Tq, Tk, H, KV, hd, pos0, q_offset,
     return load().attn_prefill_ex_fwd(q, k, v, out, lse, B, Tq, Tk, H, KV, hd, pos0, q_offset, window,
                                       float(rope_base), causal, alibi, dtype, out_dtype, workspace, workspace_bytes,
                                       stream)
+
+
+def attn_prefill_bwd_workspace_bytes(B, T, H, KV, hd, dtype, rope_base) -> int:
+    return load().attn_prefill_bwd_workspace_bytes(B, T, H, KV, hd, dtype, float(rope_base))
+
+
+def attn_prefill_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, T, H, KV, hd, pos0, rope_base, causal, alibi, dtype,
+                     out_dtype, grad_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().attn_prefill_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, T, H, KV, hd, pos0, float(rope_base),
+                                   causal, alibi, dtype, out_dtype, grad_dtype, workspace, workspace_bytes, stream)
 
 
 def attn_decode_workspace_bytes(B, H, KV, hd, Lmax) -> int:
@@ -200,6 +215,34 @@ def prefill(q, k, v, *, pos0=0, rope_base=10000.0, causal=True, alibi=ATTN_ALIBI
                                  workspace.data_ptr(), nbytes, _stream_ptr(stream))
     _check(st)
     return out, lse
+
+
+def prefill_bwd(q, k, v, out, lse, dout, *, pos0=0, rope_base=10000.0, causal=True, alibi=ATTN_ALIBI_NONE,
+                grad_dtype=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Run attn_prefill_bwd on GPU torch tensors: q [B,H,T,hd], k/v [B,KV,T,hd], the forward's out and
+    lse, and dout (same dtype as out). Returns (dq, dk, dv); ``grad_dtype`` defaults to fp32."""
+    import torch
+
+    B, H, T, hd = q.shape
+    KV = k.shape[1]
+    dt = _dtype_code(q)
+    gdt = torch.float32 if grad_dtype is None else grad_dtype
+    if dq is None:
+        dq = torch.empty(B, H, T, hd, dtype=gdt, device=q.device)
+    if dk is None:
+        dk = torch.empty(B, KV, T, hd, dtype=gdt, device=q.device)
+    if dv is None:
+        dv = torch.empty(B, KV, T, hd, dtype=gdt, device=q.device)
+    if workspace is None:
+        n = attn_prefill_bwd_workspace_bytes(B, T, H, KV, hd, dt, rope_base)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = attn_prefill_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, T, H, KV, hd, pos0, rope_base, int(causal),
+                          alibi, dt, _dtype_code(out), _dtype_code(dq), workspace.data_ptr(), nbytes,
+                          _stream_ptr(stream))
+    _check(st)
+    return dq, dk, dv
 
 
 def decode_workspace(B, H, KV, hd, Lmax, device):

@@ -214,6 +214,122 @@ int attn_prefill_ex_fwd(const void* q, const void* k, const void* v, void* out, 
 }
 
 namespace {
+// Backward workspace: [rotated K][rotated Q][D fp32], each region 256-byte
+// aligned; the rotated copies exist only when RoPE is on.
+struct BwdWs {
+  long long kr, qr, d, total;
+};
+BwdWs bwd_ws_layout(int B, int T, int H, int KV, int hd, int dtype, double rope_base) {
+  const auto up = [](long long n) { return (n + 255) / 256 * 256; };
+  const long long eb = elem_bytes(dtype);
+  const long long nk = rope_base != 0.0 ? (long long)B * KV * T * hd * eb : 0;
+  const long long nq = rope_base != 0.0 ? (long long)B * H * T * hd * eb : 0;
+  BwdWs w;
+  w.kr = 0;
+  w.qr = up(nk);
+  w.d = w.qr + up(nq);
+  w.total = w.d + up((long long)B * H * T * 4);
+  return w;
+}
+}  // namespace
+
+size_t attn_prefill_bwd_workspace_bytes(int B, int T, int H, int KV, int hd, int dtype, double rope_base) {
+  if (B <= 0 || T <= 0 || H <= 0 || KV <= 0 || hd <= 0) return 0;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return 0;
+  if ((long long)B * H * T * hd > kMaxElems) return 0;
+  return (size_t)bwd_ws_layout(B, T, H, KV, hd, dtype, rope_base).total;
+}
+
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int T, int H, int KV, int hd, int pos0,
+                     double rope_base, int causal, int alibi, int dtype, int out_dtype, int grad_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)
+    return fail(ATTN_ERR_NULL, "q, k, v, out, lse, dout, dq, dk and dv must be non-NULL");
+  if (B <= 0 || T <= 0 || H <= 0 || KV <= 0)
+    return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d T=%d H=%d KV=%d)", B, T, H, KV);
+  if (H % KV) return fail(ATTN_ERR_SHAPE, "H=%d is not a multiple of KV=%d", H, KV);
+  if (pos0 < 0 || (long long)pos0 + T > 0x7fffffffLL) return fail(ATTN_ERR_SHAPE, "pos0=%d out of range", pos0);
+  if (H > 65535 || B > 65535 || KV > 65535) return fail(ATTN_ERR_SHAPE, "H, KV and B must be <= 65535");
+  if (int c = check_common(dtype, out_dtype, alibi, rope_base, hd)) return c;
+  if (grad_dtype != ATTN_DTYPE_F32 && grad_dtype != ATTN_DTYPE_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "grad_dtype %d", grad_dtype);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_UNSUPPORTED, "causal %d", causal);
+  if ((long long)B * H * T * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "tensor too large");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(ATTN_ERR_ALIGN, "tensors must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(ATTN_ERR_ALIGN, "lse must be 4-byte aligned");
+  const BwdWs lay = bwd_ws_layout(B, T, H, KV, hd, dtype, rope_base);
+  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace of %lld bytes required", lay.total);
+  if (workspace_bytes < (size_t)lay.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes < required %lld", workspace_bytes, lay.total);
+  if (!aligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  const int bf16 = dtype == ATTN_DTYPE_BF16;
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.D = reinterpret_cast<float*>(ws + lay.d);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.KV = KV;
+  a.hd = hd;
+  a.group = H / KV;
+  a.pos0 = pos0;
+  a.causal = causal;
+  a.rope = rope_base != 0.0;
+  a.alibi = alibi;
+  a.in_bf16 = bf16;
+  a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
+  a.grad_bf16 = grad_dtype == ATTN_DTYPE_BF16;
+  a.scale = (float)(1.0 / sqrt((double)hd));
+  a.freqs = make_freqs(hd, rope_base);
+
+  if (a.rope) {  // rotated copies of K and Q, written once
+    RopeKArgs r;
+    memset(&r, 0, sizeof(r));
+    r.hd = hd;
+    r.T = T;
+    r.pos0 = pos0;
+    r.freqs = a.freqs;
+    r.k = k;
+    r.kr = ws + lay.kr;
+    r.heads = B * KV;
+    if (int c = hip_status(launch_rope_k(r, bf16, s), "rope_k launch")) return c;
+    r.k = q;
+    r.kr = ws + lay.qr;
+    r.heads = B * H;
+    if (int c = hip_status(launch_rope_k(r, bf16, s), "rope_q launch")) return c;
+    a.k = ws + lay.kr;
+    a.q = ws + lay.qr;
+  }
+  BwdPrepArgs pa;
+  pa.out = out;
+  pa.dout = dout;
+  pa.D = reinterpret_cast<float*>(ws + lay.d);
+  pa.rows = (long)B * H * T;
+  pa.hd = hd;
+  pa.out_bf16 = a.out_bf16;
+  if (int c = hip_status(launch_bwd_prep(pa, s), "backward prep launch")) return c;
+  const TimingHook tm = take_timing();
+  if (bwd_mfma_supported(a)) return hip_status(launch_bwd_mfma(a, s, tm), "backward launch");
+  if (int c = hip_status(tm.before(s), "timing event")) return c;
+  if (int c = hip_status(launch_bwd_valu(a, s), "backward launch")) return c;
+  return hip_status(tm.after(s), "timing event");
+}
+
+namespace {
 // Workspace layout (sized for the smaller split, so it fits either kernel):
 // [part_o: rows*hd fp32][part_ml: rows float2], rows = B*H*ceil(Lmax/256).
 struct DecodeWs {

@@ -67,6 +67,37 @@ struct DecodeArgs {
   RopeFreqs freqs;
 };
 
+struct BwdArgs {
+  const void* q;     // [B,H,T,hd] rotated queries (workspace) or raw when rope is off
+  const void* k;     // [B,KV,T,hd] rotated keys (workspace) or raw
+  const void* v;     // [B,KV,T,hd]
+  const void* dout;  // [B,H,T,hd] (out dtype)
+  const float* lse;  // [B,H,T] natural-log log-sum-exp from the forward
+  const float* D;    // [B,H,T] rowsum(dout * out) (workspace)
+  void* dq;          // [B,H,T,hd] (grad dtype)
+  void* dk;          // [B,KV,T,hd]
+  void* dv;          // [B,KV,T,hd]
+  int B, T, H, KV, hd, group;
+  int pos0;
+  int causal;
+  int rope;
+  int alibi;
+  int in_bf16;       // q, k, v
+  int out_bf16;      // out, dout
+  int grad_bf16;     // dq, dk, dv
+  float scale;       // 1 / sqrt(hd)
+  RopeFreqs freqs;
+};
+
+struct BwdPrepArgs {
+  const void* out;   // [rows, hd]
+  const void* dout;  // [rows, hd]
+  float* D;          // [rows]
+  long rows;
+  int hd;
+  int out_bf16;
+};
+
 // Events recorded around the main kernel of one call (either may be null).
 struct TimingHook {
   hipEvent_t start = nullptr;
@@ -80,6 +111,10 @@ hipError_t launch_prefill_valu(const PrefillArgs& a, int bf16, hipStream_t s);
 bool prefill_mfma_supported(const PrefillArgs& a, int bf16);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s, const TimingHook& tm);
+hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t s);
+hipError_t launch_bwd_valu(const BwdArgs& a, hipStream_t s);
+bool bwd_mfma_supported(const BwdArgs& a);
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t s, const TimingHook& tm);
 
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIPCC__)
