@@ -186,6 +186,7 @@ BWD_SHAPES = [
     (1, 130, 4, 4, 64, True, 1, 0.0),
     (2, 257, 8, 2, 128, False, 1, 10000.0),
     (1, 300, 16, 2, 64, True, 2, 10000.0),
+    (1, 1024, 8, 2, 128, True, 0, 500000.0),
 ]
 
 

@@ -113,6 +113,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s, const TimingHook& tm);
 hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t s);
 hipError_t launch_bwd_valu(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkv_valu(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
 bool bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t s, const TimingHook& tm);
 

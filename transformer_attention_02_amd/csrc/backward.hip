@@ -208,33 +208,33 @@ __global__ __launch_bounds__(64) void bwd_dkv_valu_kernel(BwdArgs a) {
 }
 
 template <int IBF16, int OBF16, int GBF16, int HD>
-hipError_t launch_valu_hd(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_valu_hd(const BwdArgs& a, hipStream_t s, bool dq, bool dkv) {
   const unsigned nb = (unsigned)((a.T + 63) / 64);
-  hipLaunchKernelGGL((bwd_dq_valu_kernel<IBF16, OBF16, GBF16, HD>), dim3(nb, a.H, a.B), dim3(64), 0, s, a);
-  hipLaunchKernelGGL((bwd_dkv_valu_kernel<IBF16, OBF16, GBF16, HD>), dim3(nb, a.KV, a.B), dim3(64), 0, s, a);
+  if (dq) hipLaunchKernelGGL((bwd_dq_valu_kernel<IBF16, OBF16, GBF16, HD>), dim3(nb, a.H, a.B), dim3(64), 0, s, a);
+  if (dkv) hipLaunchKernelGGL((bwd_dkv_valu_kernel<IBF16, OBF16, GBF16, HD>), dim3(nb, a.KV, a.B), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int IBF16, int OBF16, int GBF16>
-hipError_t launch_valu_g(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_valu_g(const BwdArgs& a, hipStream_t s, bool dq, bool dkv) {
   switch (a.hd) {
-    case 8: return launch_valu_hd<IBF16, OBF16, GBF16, 8>(a, s);
-    case 16: return launch_valu_hd<IBF16, OBF16, GBF16, 16>(a, s);
-    case 32: return launch_valu_hd<IBF16, OBF16, GBF16, 32>(a, s);
-    case 64: return launch_valu_hd<IBF16, OBF16, GBF16, 64>(a, s);
-    case 128: return launch_valu_hd<IBF16, OBF16, GBF16, 128>(a, s);
+    case 8: return launch_valu_hd<IBF16, OBF16, GBF16, 8>(a, s, dq, dkv);
+    case 16: return launch_valu_hd<IBF16, OBF16, GBF16, 16>(a, s, dq, dkv);
+    case 32: return launch_valu_hd<IBF16, OBF16, GBF16, 32>(a, s, dq, dkv);
+    case 64: return launch_valu_hd<IBF16, OBF16, GBF16, 64>(a, s, dq, dkv);
+    case 128: return launch_valu_hd<IBF16, OBF16, GBF16, 128>(a, s, dq, dkv);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int IBF16, int OBF16>
-hipError_t launch_valu_o(const BwdArgs& a, hipStream_t s) {
-  return a.grad_bf16 ? launch_valu_g<IBF16, OBF16, 1>(a, s) : launch_valu_g<IBF16, OBF16, 0>(a, s);
+hipError_t launch_valu_o(const BwdArgs& a, hipStream_t s, bool dq, bool dkv) {
+  return a.grad_bf16 ? launch_valu_g<IBF16, OBF16, 1>(a, s, dq, dkv) : launch_valu_g<IBF16, OBF16, 0>(a, s, dq, dkv);
 }
 
 template <int IBF16>
-hipError_t launch_valu_i(const BwdArgs& a, hipStream_t s) {
-  return a.out_bf16 ? launch_valu_o<IBF16, 1>(a, s) : launch_valu_o<IBF16, 0>(a, s);
+hipError_t launch_valu_i(const BwdArgs& a, hipStream_t s, bool dq, bool dkv) {
+  return a.out_bf16 ? launch_valu_o<IBF16, 1>(a, s, dq, dkv) : launch_valu_o<IBF16, 0>(a, s, dq, dkv);
 }
 
 }  // namespace
@@ -250,7 +250,11 @@ hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_valu(const BwdArgs& a, hipStream_t s) {
-  return a.in_bf16 ? launch_valu_i<1>(a, s) : launch_valu_i<0>(a, s);
+  return a.in_bf16 ? launch_valu_i<1>(a, s, true, true) : launch_valu_i<0>(a, s, true, true);
+}
+
+hipError_t launch_bwd_dkv_valu(const BwdArgs& a, hipStream_t s) {
+  return a.in_bf16 ? launch_valu_i<1>(a, s, false, true) : launch_valu_i<0>(a, s, false, true);
 }
 
 }  // namespace attn

@@ -35,31 +35,18 @@
 //     causal blocks first.
 #include <type_traits>
 
-#include "attn_internal.h"
+#include "mfma_tile.h"
 
 namespace attn {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using namespace tile;
 
-constexpr int BN = 64;  // keys per tile
 constexpr int NW = 8;   // waves per workgroup (two per SIMD)
 constexpr int kKAhead = 4;       // K operand reads issued ahead of the score MFMAs
 constexpr int kValuPerMfma = 8;  // softmax instructions issued per deferred V^T MFMA
 constexpr int NT = NW * 64;
-
-template <int HD>
-struct Cfg {
-  static constexpr int KCH = HD / 8;               // 16-byte chunks per key row
-  static constexpr int K_BYTES = BN * HD * 2;      // K tile, row-major [key][hd], XOR-swizzled chunks
-  static constexpr int V_BYTES = BN * HD * 2;      // V tile, row-major [key][hd], XOR-swizzled chunks
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int DMA = K_BYTES / 1024;       // 1 KiB LDS-DMA wave instructions per tensor per tile
-};
 
 struct GridMap {
   int hpw;       // heads per workgroup (1, 2 or 4)
@@ -70,95 +57,7 @@ struct GridMap {
   int xcd_aware;
 };
 
-// XOR swizzles of the 16-byte chunk index. Rows are unpadded (so one LDS-DMA
-// wave instruction fills 1 KiB of whole rows) and the swizzles keep every MFMA
-// operand read free of bank conflicts (measured: SQ_LDS_BANK_CONFLICT = 0):
-//  * K: the 16 lanes of a ds_read_b128 read one logical chunk of 16 different
-//    rows; XOR with the row's low bits sends them to 16 different chunk slots;
-//  * V: a transposing load reads rows r..r+3 x 32 bytes per 16-lane group (64
-//    bytes per 32 lanes); XOR with (r & 3) << 2 moves each row to its own
-//    64-byte bank range.
-template <int HD>
-__host__ __device__ constexpr int k_swz(int r) {
-  return HD == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int HD>
-__host__ __device__ constexpr int v_swz(int r) {
-  return HD == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
-}
-// Byte offset of logical 16-byte chunk `c` of key row `r` in the K / V tile.
-template <int HD>
-__host__ __device__ constexpr int k_off(int r, int c) { return r * HD * 2 + ((c ^ k_swz<HD>(r)) << 4); }
-template <int HD>
-__host__ __device__ constexpr int v_off(int r, int c) { return r * HD * 2 + ((c ^ v_swz<HD>(r)) << 4); }
-
-// The V swizzle depends on the row only through bits that a step of 4 rows
-// keeps, so each lane's transposing-load addresses for the rows r + 4e + 16u
-// are its row-r address plus a constant (an instruction offset).
-template <int HD>
-constexpr bool v_rows_affine() {
-  for (int r0 = 0; r0 < 12; ++r0)
-    for (int d = 0; d < 64 - 12; d += 4)
-      for (int c = 0; c < HD / 8; ++c)
-        if (v_off<HD>(r0 + d, c) != v_off<HD>(r0, c) + d * HD * 2) return false;
-  return true;
-}
-static_assert(v_rows_affine<64>() && v_rows_affine<128>(), "V swizzle must be invariant under 4-row steps");
-
-// Swap bits 2 and 3 of a row index in [0, 32).
-__device__ __forceinline__ int perm_row(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Component i (a compile-time constant after unrolling) of a uint4, without taking its address.
-__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
-
-#define LDS __attribute__((address_space(3)))
-typedef const LDS unsigned char* LdsBytes;  // operand reads address LDS directly
-
-// Direct global -> LDS staging of one K/V tile (no registers in between). Wave
-// w issues wave instructions q = w*DMA/NW .. of 1 KiB each per tensor; lane l of
-// instruction q fills LDS bytes 1024q + 16l, i.e. key row r = (1024q + 16l) /
-// (2hd) at physical chunk pc, so it fetches the logical chunk pc ^ swz(r) of
-// that row. The buffer descriptor starts at the tile and ends at the slab end:
-// rows at or past T are written as zeros.
-template <int HD>
-struct Dma {
-  using C = Cfg<HD>;
-  static constexpr int PER_WAVE = C::DMA / NW;
-  static_assert(C::DMA % NW == 0, "every wave issues the same share of a tile");
-  int koff[PER_WAVE];  // per-lane source byte offsets within the tile
-  int voff[PER_WAVE];
-
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int p = 1024 * (wave * PER_WAVE + i) + 16 * lane;
-      const int r = p / (HD * 2), pc = (p % (HD * 2)) / 16;
-      koff[i] = (r * HD + (pc ^ k_swz<HD>(r)) * 8) * 2;
-      voff[i] = (r * HD + (pc ^ v_swz<HD>(r)) * 8) * 2;
-    }
-  }
-
-  __device__ __forceinline__ void issue(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, unsigned char* stage,
-                                        int wave) const {
-    const int bytes = (T - kt * BN) * HD * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)kt * BN * HD, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)kt * BN * HD, bytes);
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int q = wave * PER_WAVE + i;
-#if defined(__HIP_DEVICE_COMPILE__)  // (the host pass drops the kernel stubs of later instantiations otherwise)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(stage + 1024 * q), 16, koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(stage + C::K_BYTES + 1024 * q), 16, voff[i], 0, 0, 0);
-#endif
-    }
-  }
-};
 
 // One wave's online-softmax state for 32 query rows (lane n holds row qi, the
 // two half-waves split the keys of a tile), and the steps of one 64-key tile.
@@ -397,7 +296,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   const int kt_begin = WINDOW ? max(0, tq0 - a.window + 1) / BN : 0;
 
   // The first K/V tile streams into stage 0 during the Q set-up.
-  Dma<HD> dma;
+  Dma<HD, NW> dma;
   dma.init(wave, lane);
   dma.issue(Kg, Vg, kt_begin, a.Tk, s0, wave);
   // Stage 2 stands in for the tile before the first one: its V part is zeroed
