@@ -16,8 +16,13 @@ kernel on its own stream; ``decode.roofline`` is the same for the split-KV
 kernel. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
 same workload.
 
+``--workload backward`` times attn_prefill_bwd on the Llama-3-8B prefill
+instead (bf16 gradients; ``value`` = backward TFLOP/s with the algorithmic
+10*B*H*hd*T(T+1)/2 flops; ``roofline`` covers its two matrix-core kernels,
+dq and dk/dv, timed together).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload all|prefill|decode|alibi|small|window|chunk|copy]
+                       [--workload all|prefill|decode|alibi|small|window|chunk|backward|copy]
                        [--no-cpu-baseline] [--no-ceilings]
 """
 from __future__ import annotations
@@ -164,6 +169,36 @@ class Decode:
         return self.w.kv_read_bytes()
 
 
+class Backward:
+    """attn_prefill_bwd on the forward's own out/lse (computed once, untimed)."""
+
+    def __init__(self, w, dev, bd, W, torch, stream):
+        self.w, self.bd = w, bd
+        self.fwd = Prefill(w, dev, bd, W, torch)
+        self.fwd(stream)
+        self.dout = W.prefill_dout(w).to(dev)
+        shp_q, shp_k = (w.B, w.H, w.T, w.hd), (w.B, w.KV, w.T, w.hd)
+        self.dq = torch.empty(shp_q, dtype=torch.bfloat16, device=dev)
+        self.dk = torch.empty(shp_k, dtype=torch.bfloat16, device=dev)
+        self.dv = torch.empty(shp_k, dtype=torch.bfloat16, device=dev)
+        self.ws_bytes = bd.attn_prefill_bwd_workspace_bytes(w.B, w.T, w.H, w.KV, w.hd, self.fwd.dt, w.rope_base)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream, events=None):
+        w, bd, f = self.w, self.bd, self.fwd
+        if events:
+            bd.attn_set_timing_events(*events)
+        st = bd.attn_prefill_bwd(f.q.data_ptr(), f.k.data_ptr(), f.v.data_ptr(), f.out.data_ptr(), f.lse.data_ptr(),
+                                 self.dout.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
+                                 w.B, w.T, w.H, w.KV, w.hd, w.pos0, w.rope_base, int(w.causal), w.alibi, f.dt,
+                                 bd.ATTN_DTYPE_BF16, bd.ATTN_DTYPE_BF16, self.ws.data_ptr(), self.ws_bytes, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_prefill_bwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+    def work(self):
+        return self.w.bwd_flops()
+
+
 def cpu_baseline_leg(pre, dec, heads, seqs):
     """The fp64 oracle on a bounded sample of the same workload (rank 0, N=1 only)."""
     import numpy as np
@@ -214,19 +249,47 @@ def cpu_baseline_leg(pre, dec, heads, seqs):
     return res
 
 
+def cpu_baseline_bwd(bwd, heads):
+    """The fp64 oracle backward on a bounded sample: the first ``heads`` query
+    heads (whole GQA groups) of batch 0, all rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_prefill_bwd
+
+    w, f = bwd.w, bwd.fwd
+    g = w.H // w.KV
+    heads = max(g, heads // g * g)
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    qs, ks, vs = f64(f.q[0:1, :heads]), f64(f.k[0:1, :heads // g]), f64(f.v[0:1, :heads // g])
+    t0 = time.perf_counter()
+    dq, _, _ = attention_prefill_bwd(qs, ks, vs, f64(bwd.dout[0:1, :heads]), pos0=w.pos0, rope_base=w.rope_base,
+                                     causal=w.causal, alibi=w.alibi)
+    dt = time.perf_counter() - t0
+    flops = 10.0 * heads * w.hd * w.pairs()
+    err = float(np.abs(f64(bwd.dq[0:1, :heads]) - dq).max())
+    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": flops / dt / 1e12,
+            "unit": "TFLOP/s", "seconds": dt,
+            "sample": f"{heads} query heads of batch 0 ({heads // g} KV heads), all {w.T} rows: "
+                      f"{flops / w.bwd_flops() * 100:.2f}% of the backward step",
+            "max_abs_err_dq_vs_gpu_bf16": err}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "alibi", "small", "window", "chunk", "copy"],
+                    choices=["all", "prefill", "decode", "alibi", "small", "window", "chunk", "backward", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the same-run library GEMM that gives the practical bf16 matrix-core ceiling")
     ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--cpu-seqs", type=int, default=64)
+    ap.add_argument("--cpu-heads-bwd", type=int, default=4)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -268,18 +331,22 @@ def main():
              "window": W.LLAMA3_WINDOW, "chunk": W.LLAMA3_CHUNK}.get(args.workload)
     pre = Prefill(pre_w, dev, bd, W, torch) if pre_w is not None else None
     dec = Decode(W.KV_DECODE, dev, bd, W, torch) if args.workload in ("all", "decode") else None
-    log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None}")
-
     stream = torch.cuda.current_stream().cuda_stream
+    bwd = Backward(W.LLAMA3_8B, dev, bd, W, torch, stream) if args.workload == "backward" else None
+    log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None} "
+        f"backward={bwd.w.name if bwd else None}")
+
     for _ in range(args.warmup):
         if pre:
             pre(stream)
         if dec:
             dec(stream)
+        if bwd:
+            bwd(stream)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk")}
+    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk")}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
@@ -292,6 +359,10 @@ def main():
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][0]), ctypes.c_void_p(stream))
             dec(stream, ev["dk"][i])
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][1]), ctypes.c_void_p(stream))
+        if bwd:
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["bc"][i][0]), ctypes.c_void_p(stream))
+            bwd(stream, ev["bk"][i])
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["bc"][i][1]), ctypes.c_void_p(stream))
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -342,6 +413,20 @@ def main():
             cfg["workload"] = w.name
         else:
             cfg["workload"] = cfg["workload"] + " + " + w.name
+    if bwd:
+        w = bwd.w
+        bc, bk = avg("bc"), avg("bk")
+        tflops = w.bwd_flops() / (bc * 1e-3) / 1e12
+        kt = w.bwd_flops() / (bk * 1e-3) / 1e12
+        line.update(value=tflops, unit="TFLOP/s", metric="causal GQA+RoPE attn bwd TFLOP/s (prefill), 1 GPU")
+        cfg["workload"] = "backward of " + w.name
+        cfg["backward"] = {"B": w.B, "T": w.T, "H": w.H, "KV": w.KV, "hd": w.hd, "rope_base": w.rope_base,
+                           "causal": w.causal, "grad_dtype": "bf16", "flops": w.bwd_flops(), "call_ms": bc,
+                           "kernels_ms": bk}
+        cfg["backward"]["kernels_ms_median"], cfg["backward"]["kernels_ms_min"] = med_min("bk")
+        line["roofline"] = {"bound": "mfma", "achieved": kt, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": kt / PEAK_BF16_TFLOPS, "traffic": None,
+                            "kernel": f"bwd_dq_mfma_kernel<{w.hd}> + bwd_dkv_mfma_kernel<{w.hd}> (timed together)"}
     line["config"] = cfg
     torch.cuda.synchronize()
     ok = True
@@ -349,10 +434,13 @@ def main():
         ok &= bool(torch.isfinite(pre.out).all().item())
     if dec:
         ok &= bool(torch.isfinite(dec.out).all().item())
+    if bwd:
+        for t in (bwd.dq, bwd.dk, bwd.dv):
+            ok &= bool(torch.isfinite(t).all().item())
     line["outputs_finite"] = ok
     hip.close()
 
-    if pre and not args.no_ceilings:
+    if (pre or bwd) and not args.no_ceilings:
         # Same-run context for the matrix-core roofline: the vendor GEMM (torch.matmul ->
         # hipBLASLt) on N(0,1) bf16 operands. The published 2.5 PFLOP/s assumes the 2.4 GHz
         # peak clock; with random data the chip runs power-limited well below it.
@@ -375,7 +463,10 @@ def main():
                                      "prefill_kernel_vs_gemm": line["roofline"]["achieved"] / gemm}
         del a_, b_, c_
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and bwd:
+        log("cpu baseline: timing the fp64 oracle backward on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_bwd(bwd, args.cpu_heads_bwd)
+    elif not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline_leg(pre, dec, args.cpu_heads, args.cpu_seqs)
     else:

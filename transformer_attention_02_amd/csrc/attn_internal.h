@@ -115,6 +115,7 @@ hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t s);
 hipError_t launch_bwd_valu(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkv_valu(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkv_mfma(const BwdArgs& a, hipStream_t s);
 bool bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t s, const TimingHook& tm);
 

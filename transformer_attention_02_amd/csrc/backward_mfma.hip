@@ -170,7 +170,7 @@ void bwd_dq_mfma_kernel(BwdArgs a, DqGrid gm) {
   const int q_last = min(a.T, q0 + gm.bm) - 1;
   const int nkt = CAUSAL ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
 
-  Dma<HD, QW, true, true> dma;
+  Dma<HD, QW, SWZ_V, SWZ_K> dma;
   dma.init(wave, lane);
   dma.issue(Kg, Vg, 0, a.T, s0, wave);
 
@@ -286,6 +286,322 @@ void launch_dq_hd(const BwdArgs& a, hipStream_t s) {
   }
 }
 
+// --------------------------------------------------------------- dk/dv kernel
+// 16 keys per wave on v_mfma_f32_16x16x32_bf16, so that a wave's state (dK'^T
+// and dV^T for its keys, their K'/V operands) stays near 100 registers and two
+// waves share each SIMD.
+constexpr int KW = 8;        // waves per dk/dv workgroup
+constexpr int KT = KW * 64;
+constexpr int KB = 16 * KW;  // keys per workgroup
+
+struct DkvGrid {
+  int nkb;    // key blocks of KB keys
+  int units;  // B * KV
+  int xcd_aware;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Transposing read of a 16x32 A operand (16 columns of the tile: one 16-dim
+// block; 32 rows: queries 8g .. 8g+7 of each 16-lane group g, four per load).
+__device__ __forceinline__ bf16x8 read_tr32(LdsBytes p, int second) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p + second));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int HD, bool ALIBI, bool CAUSAL>
+struct DkvWave {
+  f32x4 dk[HD / 16];   // dK'^T block b: lane holds key l%16, dims 16b + 4g + i
+  f32x4 dv[HD / 16];   // dV^T, same layout
+  bf16x8 kf[HD / 32];  // K'^T B operand, k-step s: dims 32s + 8g .. +7 of key l%16
+  bf16x8 vf[HD / 32];  // V^T B operand
+  float c2, slope2;
+  int kk, kw0, T, lane;
+  int rbase;             // byte offset of this lane's operand row (chunk part excluded)
+  int rsw;               // its swizzle
+  int tro[HD / 16];      // transposing-read offsets, one per 16-dim block
+
+  __device__ __forceinline__ void init_offsets() {
+    const int l16 = lane & 15, g = lane >> 4;
+    // S / dP rows: query 8(l16/4) + l16%4 of each 32-query chunk (+4 for the
+    // second 16-row block), so that block 0 / 1 registers hold queries
+    // 8g .. 8g+3 / 8g+4 .. 8g+7 of the chunk: the B operand of dV^T, dK'^T
+    const int r = 8 * (l16 >> 2) + (l16 & 3);
+    rbase = r * HD * 2;
+    rsw = q_swz<HD>(r);
+    const int rt = 8 * g + (l16 >> 2);
+#pragma unroll
+    for (int bb = 0; bb < HD / 16; ++bb) {
+      const int col = 16 * bb + 4 * (l16 & 3);
+      int o = q_off<HD>(rt, col >> 3) + (col & 7) * 2;
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("" : "+v"(o));
+#endif
+      tro[bb] = o;
+    }
+  }
+
+  // One 64-row query tile starting at query q0: Q' at qb and dO at gb (query
+  // swizzle), the rows' lse and D at lb / db (64 floats each). Operand reads
+  // run a few ahead of the matrix-core instructions that consume them
+  // (scheduling groups), so LDS latency hides behind the MFMA chain.
+  template <bool MASK>
+  __device__ __forceinline__ void tile(LdsBytes qb, LdsBytes gb, LdsBytes lb, LdsBytes db, int q0) {
+    constexpr int NS = HD / 32;  // k-steps of the S / dP contractions
+    constexpr int NB = HD / 16;  // 16-dim blocks of dK'^T / dV^T
+    const int g = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // (causal) every query of the chunk precedes every key of the wave
+      if (MASK && CAUSAL && q0 + 32 * c + 31 < kw0) continue;
+      // S = Q' K'^T and dP = dO V^T for the chunk's two 16-row blocks
+      bf16x8 oq[2][NS], og[2][NS];
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int o = rbase + (32 * c + 4 * b) * HD * 2 + (((4 * st + g) ^ rsw) << 4);
+          oq[b][st] = *reinterpret_cast<const LDS bf16x8*>(qb + o);
+          og[b][st] = *reinterpret_cast<const LDS bf16x8*>(gb + o);
+        }
+      const int r0 = 32 * c + 8 * g;
+      const f32x4 la = *reinterpret_cast<const LDS f32x4*>(lb + 4 * r0);
+      const f32x4 lc = *reinterpret_cast<const LDS f32x4*>(lb + 4 * r0 + 16);
+      const f32x4 da = *reinterpret_cast<const LDS f32x4*>(db + 4 * r0);
+      const f32x4 dc = *reinterpret_cast<const LDS f32x4*>(db + 4 * r0 + 16);
+      f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oq[b][st], kf[st], s[b], 0, 0, 0);
+          dp[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(og[b][st], vf[st], dp[b], 0, 0, 0);
+        }
+      // 4 reads ahead, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * NS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // lse and D
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+      // register i of block b is query q0 + 32c + 8g + 4b + i
+      const int dbase = kk - (q0 + r0);  // key - query at j = 0
+      const float dbf = (float)dbase;
+      float p[8], ds[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float sv = s[j / 4][j % 4], dpv = dp[j / 4][j % 4];
+        const float lse = j < 4 ? la[j] : lc[j - 4];
+        const float dd = j < 4 ? da[j] : dc[j - 4];
+        float t;
+        if constexpr (ALIBI) {
+          const float bias = CAUSAL ? fmaf(-slope2, (float)j, slope2 * dbf) : -slope2 * fabsf(dbf - (float)j);
+          t = fmaf(sv, c2, bias);
+        } else {
+          t = sv * c2;
+        }
+        if constexpr (MASK) {
+          const bool vis = (q0 + r0 + j < T) && (!CAUSAL || dbase <= j);
+          t = vis ? t : -INFINITY;
+        }
+        p[j] = __builtin_amdgcn_exp2f(fmaf(lse, -kLog2eM, t));
+        ds[j] = p[j] * (dpv - dd);
+      }
+      const bf16x8 pb = pack8(p), dsb = pack8(ds);
+      // dV^T += dO^T P and dK'^T += Q'^T dS, one 16-dim block at a time
+      bf16x8 tg[NB], tq[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const int o = tro[bb] + 32 * c * HD * 2;
+        tg[bb] = read_tr32(gb + o, 4 * HD * 2);
+        tq[bb] = read_tr32(qb + o, 4 * HD * 2);
+      }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        dv[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tg[bb], pb, dv[bb], 0, 0, 0);
+        dk[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tq[bb], dsb, dk[bb], 0, 0, 0);
+      }
+      // 8 transposing reads (4 operands) ahead, then two per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NB - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+  }
+};
+
+// 64 floats of one row vector (lse or D) straight into LDS; rows at or past
+// `rows` read as zero.
+__device__ __forceinline__ void dma_row64(const float* g, int rows, unsigned char* dst, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(g, rows * 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)dst, 4, 4 * lane, 0, 0, 0);
+#endif
+}
+
+template <int HD, bool ALIBI, bool CAUSAL, bool GRAD_BF16>
+__global__ __launch_bounds__(KT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_mfma_kernel(BwdArgs a, DkvGrid gm) {
+  using C = Cfg<HD>;
+  constexpr int SB = C::STAGE + 512;  // Q' tile, dO tile, 64 lse, 64 D
+  __shared__ __attribute__((aligned(16))) unsigned char s0[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char s1[SB];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
+
+  // The key blocks of one (batch, KV head) run side by side on one XCD,
+  // heaviest (earliest, under the causal mask) first, and all of them stream
+  // the query tiles in the same order, so each tile is fetched into that XCD's
+  // L2 once for all of them.
+  const int w = blockIdx.x;
+  int unit, kblk;
+  if (gm.xcd_aware) {
+    const int upx = gm.units >> 3;
+    const int j = w >> 3;
+    unit = (w & 7) * upx + j / gm.nkb;
+    kblk = j % gm.nkb;
+  } else {
+    unit = w / gm.nkb;
+    kblk = w % gm.nkb;
+  }
+  const int kvh = unit % a.KV;
+  const int b = unit / a.KV;
+  const int kb0 = kblk * KB;
+  const int qt_lo = CAUSAL ? kb0 / BN : 0;
+  const int nqt = (a.T + BN - 1) / BN;
+  const int nq = nqt - qt_lo;
+  const int total = a.group * nq;
+
+  Dma<HD, KW, SWZ_Q, SWZ_Q> dma;
+  dma.init(wave, lane);
+  // tile idx: query tile nqt-1-idx/group (last first) of head idx%group
+  auto issue = [&](int idx, unsigned char* stage) __attribute__((always_inline)) {
+    const int hh = idx % a.group, qt = nqt - 1 - idx / a.group;
+    const long hrow = ((long)b * a.H + kvh * a.group + hh) * a.T;
+    dma.issue(reinterpret_cast<const uint16_t*>(a.q) + hrow * HD, reinterpret_cast<const uint16_t*>(a.dout) + hrow * HD,
+              qt, a.T, stage, wave);
+    if (wave == 0) dma_row64(a.lse + hrow + qt * BN, a.T - qt * BN, stage + C::STAGE, lane);
+    if (wave == 1) dma_row64(a.D + hrow + qt * BN, a.T - qt * BN, stage + C::STAGE + 256, lane);
+  };
+  issue(0, s0);
+
+  DkvWave<HD, ALIBI, CAUSAL> ws;
+  ws.kw0 = kb0 + 16 * wave;
+  ws.kk = ws.kw0 + (lane & 15);
+  ws.T = a.T;
+  ws.lane = lane;
+  ws.c2 = a.scale * kLog2eM;
+  ws.slope2 = 0.f;  // per query head: set for each tile
+  ws.init_offsets();
+  const long krow = ((long)b * a.KV + kvh) * a.T + min(ws.kk, a.T - 1);
+  {
+    const uint4* ks = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k) + krow * HD);
+    const uint4* vs = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.v) + krow * HD);
+#pragma unroll
+    for (int st = 0; st < HD / 32; ++st) {
+      ws.kf[st] = as_bf16x8(ks[4 * st + g]);
+      ws.vf[st] = as_bf16x8(vs[4 * st + g]);
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < HD / 16; ++bb) ws.dk[bb] = ws.dv[bb] = f32x4{};
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  auto step = [&](int idx, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int P = decltype(par_tag)::value;
+    unsigned char* cur = P ? s1 : s0;
+    unsigned char* nxt = P ? s0 : s1;
+    if (idx + 1 < total) issue(idx + 1, nxt);
+    const int q0 = (nqt - 1 - idx / a.group) * BN;
+    if constexpr (ALIBI) ws.slope2 = alibi_slope(a.alibi, kvh * a.group + idx % a.group, a.H) * kLog2eM;
+    ws.template tile<MASK>((LdsBytes)cur, (LdsBytes)(cur + C::K_BYTES), (LdsBytes)(cur + C::STAGE),
+                           (LdsBytes)(cur + C::STAGE + 256), q0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  // a tile needs the mask when it reaches the diagonal of the key block or
+  // the end of the sequence
+  auto masked = [&](int idx) __attribute__((always_inline)) {
+    const int q0 = (nqt - 1 - idx / a.group) * BN;
+    return (CAUSAL && q0 < kb0 + KB) || q0 + BN > a.T;
+  };
+  for (int idx = 0; idx < total; idx += 2) {
+    if (masked(idx)) step(idx, std::true_type{}, Even{});
+    else step(idx, std::false_type{}, Even{});
+    if (idx + 1 >= total) break;
+    if (masked(idx + 1)) step(idx + 1, std::true_type{}, Odd{});
+    else step(idx + 1, std::false_type{}, Odd{});
+  }
+
+  if (ws.kk >= a.T) return;
+  const int pos = a.pos0 + ws.kk;
+#pragma unroll
+  for (int bb = 0; bb < HD / 16; ++bb) {
+    const int d = 16 * bb + 4 * g;
+    float y[4], z[4];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float x0 = ws.dk[bb][e] * a.scale, x1 = ws.dk[bb][e + 1] * a.scale;
+      float c = 1.f, sn = 0.f;
+      if (a.rope) rope_cos_sin(pos, a.freqs.rev[(d + e) >> 1], c, sn);
+      y[e] = rot0(x0, x1, c, -sn);
+      y[e + 1] = rot1(x0, x1, c, -sn);
+      z[e] = ws.dv[bb][e];
+      z[e + 1] = ws.dv[bb][e + 1];
+    }
+    const long o = krow * HD + d;
+    if constexpr (GRAD_BF16) {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.dk) + o) =
+          make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.dv) + o) =
+          make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.dk) + o) = make_float4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.dv) + o) = make_float4(z[0], z[1], z[2], z[3]);
+    }
+  }
+}
+
+DkvGrid make_dkv_grid(const BwdArgs& a) {
+  DkvGrid gm;
+  gm.nkb = (a.T + KB - 1) / KB;
+  gm.units = a.B * a.KV;
+  gm.xcd_aware = (gm.units % 8) == 0;
+  return gm;
+}
+
+template <int HD, bool ALIBI, bool CAUSAL>
+void launch_dkv_g(const BwdArgs& a, hipStream_t s) {
+  const DkvGrid gm = make_dkv_grid(a);
+  const dim3 grid((unsigned)(gm.units * gm.nkb));
+  if (a.grad_bf16) {
+    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<HD, ALIBI, CAUSAL, true>), grid, dim3(KT), 0, s, a, gm);
+  } else {
+    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<HD, ALIBI, CAUSAL, false>), grid, dim3(KT), 0, s, a, gm);
+  }
+}
+
+template <int HD>
+void launch_dkv_hd(const BwdArgs& a, hipStream_t s) {
+  if (a.alibi) {
+    if (a.causal) launch_dkv_g<HD, true, true>(a, s);
+    else launch_dkv_g<HD, true, false>(a, s);
+  } else {
+    if (a.causal) launch_dkv_g<HD, false, true>(a, s);
+    else launch_dkv_g<HD, false, false>(a, s);
+  }
+}
+
 }  // namespace
 
 bool bwd_mfma_supported(const BwdArgs& a) {
@@ -304,6 +620,15 @@ hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_dkv_mfma(const BwdArgs& a, hipStream_t s) {
+  if (a.hd == 128) {
+    launch_dkv_hd<128>(a, s);
+  } else {
+    launch_dkv_hd<64>(a, s);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace attn
 
 namespace attn {
@@ -312,7 +637,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t s, const TimingHook& tm
   hipError_t e = tm.before(s);
   if (e != hipSuccess) return e;
   if ((e = launch_bwd_dq_mfma(a, s)) != hipSuccess) return e;
-  if ((e = launch_bwd_dkv_valu(a, s)) != hipSuccess) return e;
+  if ((e = launch_bwd_dkv_mfma(a, s)) != hipSuccess) return e;
   return tm.after(s);
 }
 

@@ -73,14 +73,36 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
 #define LDS __attribute__((address_space(3)))
 typedef const LDS unsigned char* LdsBytes;  // operand reads address LDS directly
 
-// Direct global -> LDS staging of one K/V tile (no registers in between). Wave
-// w of NWAVES issues wave instructions q = w*DMA/NWAVES .. of 1 KiB each per
-// tensor; lane l of instruction q fills LDS bytes 1024q + 16l, i.e. key row
-// r = (1024q + 16l) / (2hd) at physical chunk pc, so it fetches the logical
-// chunk pc ^ swz(r) of that row (KSWZ / VSWZ pick the K or V swizzle for each
-// tensor). The buffer descriptor starts at the tile and ends at the slab end:
-// rows at or past T are written as zeros.
-template <int HD, int NWAVES, bool K_IS_VSWZ = false, bool V_IS_KSWZ = false>
+// Swizzle of the query-row tiles of the dk/dv backward kernel (Q' and dO,
+// 64 rows), read two ways by 16x16x32 operands: as rows (the 16 lanes of a
+// ds_read_b128 read one logical chunk of rows {8a + 4b + j : a, j in 0..3})
+// and transposed (a ds_read_b64_tr_b16 per 16-lane group g reads rows
+// 8g .. 8g+3 x 32 bytes). It depends on row bits 0, 1, 3 and 4 only: a lane's
+// second transposing load is 4 rows down and the tile's two 32-row halves are
+// addressed by a constant step. Picked among XOR swizzles of those bits by
+// measuring SQ_LDS_BANK_CONFLICT for both patterns on gfx950: zero for both.
+template <int HD>
+__host__ __device__ constexpr int q_swz(int r) {
+  return HD == 128 ? ((r & 1) | ((r & 1) << 1) | ((((r >> 1) ^ (r >> 4)) & 1) << 2) | (((r >> 3) & 1) << 3))
+                   : ((r & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2));
+}
+template <int HD>
+__host__ __device__ constexpr int q_off(int r, int c) { return r * HD * 2 + ((c ^ q_swz<HD>(r)) << 4); }
+
+enum Swz { SWZ_K = 0, SWZ_V = 1, SWZ_Q = 2 };
+template <int HD, int KIND>
+__host__ __device__ constexpr int swz(int r) {
+  return KIND == SWZ_K ? k_swz<HD>(r) : (KIND == SWZ_V ? v_swz<HD>(r) : q_swz<HD>(r));
+}
+
+// Direct global -> LDS staging of one 64-row tile of two tensors (K/V, or Q'/dO
+// in the backward), with no registers in between. Wave w of NWAVES issues wave
+// instructions q = w*DMA/NWAVES .. of 1 KiB each per tensor; lane l of
+// instruction q fills LDS bytes 1024q + 16l, i.e. row r = (1024q + 16l) / (2hd)
+// at physical chunk pc, so it fetches the logical chunk pc ^ swz(r) of that row
+// (SW0 / SW1 pick the swizzle of each tensor). The buffer descriptor starts at
+// the tile and ends at the slab end: rows at or past T are written as zeros.
+template <int HD, int NWAVES, int SW0 = SWZ_K, int SW1 = SWZ_V>
 struct Dma {
   using C = Cfg<HD>;
   static constexpr int PER_WAVE = C::DMA / NWAVES;
@@ -93,8 +115,8 @@ struct Dma {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int p = 1024 * (wave * PER_WAVE + i) + 16 * lane;
       const int r = p / (HD * 2), pc = (p % (HD * 2)) / 16;
-      koff[i] = (r * HD + (pc ^ (K_IS_VSWZ ? v_swz<HD>(r) : k_swz<HD>(r))) * 8) * 2;
-      voff[i] = (r * HD + (pc ^ (V_IS_KSWZ ? k_swz<HD>(r) : v_swz<HD>(r))) * 8) * 2;
+      koff[i] = (r * HD + (pc ^ swz<HD, SW0>(r)) * 8) * 2;
+      voff[i] = (r * HD + (pc ^ swz<HD, SW1>(r)) * 8) * 2;
     }
   }
 

@@ -64,6 +64,11 @@ class PrefillWorkload:
         """Algorithmic flops: two contractions over the visible (query, key) pairs."""
         return 4.0 * self.B * self.H * self.hd * self.pairs()
 
+    def bwd_flops(self) -> float:
+        """Algorithmic flops of the backward: five contractions over the visible
+        pairs (the scores again, dP, dV, dK and dQ), 2.5 times the forward."""
+        return 10.0 * self.B * self.H * self.hd * self.pairs()
+
     def io_bytes(self, out_elem: int = 4) -> int:
         e = 4 if self.dtype == F32 else 2
         return (self.B * self.H * self.T * self.hd * (e + out_elem)
@@ -176,6 +181,16 @@ def prefill_inputs(w: PrefillWorkload, *, B: int | None = None, T: int | None = 
     if w.Tq:  # a chunk: the query rows of those tokens, drawn with the whole prompt
         q = q[:, :, w.q_offset:w.q_offset + w.Tq].contiguous()
     return q, k, v
+
+
+def prefill_dout(w: PrefillWorkload, *, B: int | None = None, T: int | None = None):
+    """Host tensor dout [B,H,rows,hd]: the upstream gradient for a backward
+    step, N(0,1) rounded like the inputs, from its own seed (w.seed + 1000)."""
+    B = w.B if B is None else B
+    T = w.rows if T is None else T
+    g = torch.Generator().manual_seed(w.seed + 1000)
+    draw = normal_bf16 if w.dtype == BF16 else normal_f32
+    return draw(g, (B, w.H, T, w.hd))
 
 
 def random_prefill(seed: int, B: int, T: int, H: int, KV: int, hd: int, dtype: str = BF16, scale: float = 1.0):
