@@ -289,7 +289,7 @@ def main():
                     help="skip the same-run library GEMM that gives the practical bf16 matrix-core ceiling")
     ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--cpu-seqs", type=int, default=64)
-    ap.add_argument("--cpu-heads-bwd", type=int, default=4)
+    ap.add_argument("--cpu-heads-bwd", type=int, default=16)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

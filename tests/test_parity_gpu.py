@@ -187,6 +187,9 @@ BWD_SHAPES = [
     (2, 257, 8, 2, 128, False, 1, 10000.0),
     (1, 300, 16, 2, 64, True, 2, 10000.0),
     (1, 1024, 8, 2, 128, True, 0, 500000.0),
+    (1, 1, 4, 1, 128, True, 1, 10000.0),    # one token: dq = dk = 0, dv = dout summed over the group
+    (1, 64, 4, 2, 64, False, 0, 10000.0),   # exactly one tile
+    (2, 200, 2, 2, 128, True, 0, 10000.0),  # MHA, several batches, ragged tail
 ]
 
 
@@ -217,6 +220,43 @@ def test_backward_shapes(shape, dtype):
     g = torch.Generator().manual_seed(4000 + T)
     dout = torch.randn(B, H, T, hd, generator=g).to(dtype)
     check_backward(q, k, v, dout, causal, alibi, base, label=str(shape))
+
+
+def test_backward_bf16_gradients():
+    """bf16 gradient output: the fp32-gradient result rounded once (RNE)."""
+    q, k, v = W.random_prefill(77, 1, 300, 8, 2, 128)
+    dout = torch.randn(1, 8, 300, 128, generator=torch.Generator().manual_seed(78)).to(torch.bfloat16)
+    out, lse = gpu_prefill(q, k, v, rope_base=10000.0, out_dtype=torch.bfloat16)
+    g32 = bd.prefill_bwd(q.cuda(), k.cuda(), v.cuda(), out, lse, dout.cuda(), rope_base=10000.0)
+    g16 = bd.prefill_bwd(q.cuda(), k.cuda(), v.cuda(), out, lse, dout.cuda(), rope_base=10000.0,
+                         grad_dtype=torch.bfloat16)
+    for a, b in zip(g32, g16):
+        assert b.dtype == torch.bfloat16
+        assert torch.equal(a.to(torch.bfloat16), b)
+
+
+def test_backward_full_size_sampled():
+    """The Llama-3-8B backward exactly as bench.py runs it (bf16 in/out/gradients, one
+    launch over all heads); batch 0's first KV group (its 4 query heads) against the oracle."""
+    w = W.LLAMA3_8B
+    print(f"[full-size backward] {w.name}", flush=True)
+    q, k, v = W.prefill_inputs(w)
+    dout = W.prefill_dout(w)
+    out, lse = gpu_prefill(q, k, v, pos0=w.pos0, rope_base=w.rope_base, causal=w.causal,
+                           out_dtype=torch.bfloat16)
+    dq, dk, dv = bd.prefill_bwd(q.cuda(), k.cuda(), v.cuda(), out, lse, dout.cuda(), pos0=w.pos0,
+                                rope_base=w.rope_base, causal=w.causal, grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all().item()
+    g = w.H // w.KV
+    rq, rk, rv = attention_prefill_bwd(to64(q[0:1, :g]), to64(k[0:1, :1]), to64(v[0:1, :1]), to64(dout[0:1, :g]),
+                                       pos0=w.pos0, rope_base=w.rope_base, causal=w.causal)
+    for name, got, ref in (("dq", dq[0:1, :g], rq), ("dk", dk[0:1, :1], rk), ("dv", dv[0:1, :1], rv)):
+        err = np.abs(to64(got) - ref).max()
+        scale = max(1.0, np.abs(ref).max())
+        print(f"  {name}: max abs err {err:.3g} (gradient scale {scale:.3g})", flush=True)
+        assert err <= GRAD_TOL[torch.bfloat16] * scale, (name, err, scale)
 
 
 def test_backward_lab_instance():

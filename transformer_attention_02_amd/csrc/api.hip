@@ -275,6 +275,7 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* ou
   a.k = k;
   a.v = v;
   a.dout = dout;
+  a.out = out;
   a.lse = lse;
   a.D = reinterpret_cast<float*>(ws + lay.d);
   a.dq = dq;
@@ -314,6 +315,10 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* ou
     a.k = ws + lay.kr;
     a.q = ws + lay.qr;
   }
+  const TimingHook tm = take_timing();
+  // the matrix-core dq kernel computes D itself (its rows' dout are already in
+  // registers); the vector-ALU kernels take it from a pre-pass
+  if (bwd_mfma_supported(a)) return hip_status(launch_bwd_mfma(a, s, tm), "backward launch");
   BwdPrepArgs pa;
   pa.out = out;
   pa.dout = dout;
@@ -322,8 +327,6 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* ou
   pa.hd = hd;
   pa.out_bf16 = a.out_bf16;
   if (int c = hip_status(launch_bwd_prep(pa, s), "backward prep launch")) return c;
-  const TimingHook tm = take_timing();
-  if (bwd_mfma_supported(a)) return hip_status(launch_bwd_mfma(a, s, tm), "backward launch");
   if (int c = hip_status(tm.before(s), "timing event")) return c;
   if (int c = hip_status(launch_bwd_valu(a, s), "backward launch")) return c;
   return hip_status(tm.after(s), "timing event");

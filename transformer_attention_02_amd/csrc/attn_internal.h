@@ -73,7 +73,8 @@ struct BwdArgs {
   const void* v;     // [B,KV,T,hd]
   const void* dout;  // [B,H,T,hd] (out dtype)
   const float* lse;  // [B,H,T] natural-log log-sum-exp from the forward
-  const float* D;    // [B,H,T] rowsum(dout * out) (workspace)
+  const void* out;   // [B,H,T,hd] forward output (out_dtype)
+  float* D;          // [B,H,T] rowsum(dout * out) (workspace)
   void* dq;          // [B,H,T,hd] (grad dtype)
   void* dk;          // [B,KV,T,hd]
   void* dv;          // [B,KV,T,hd]

@@ -50,7 +50,7 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[HD / 32]) {
 #pragma unroll
   for (int mb = 0; mb < HD / 32; ++mb) {
     const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-    int o = v_off<HD>(8 * hf + (li >> 2), col >> 3) + (col & 7) * 2;
+    int o = kt_off<HD>(8 * hf + (li >> 2), col >> 3) + (col & 7) * 2;
 #if defined(__HIP_DEVICE_COMPILE__)
     asm volatile("" : "+v"(o));
 #endif
@@ -60,12 +60,13 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[HD / 32]) {
 
 // A^T operand of 16 rows (16u .. 16u+15 of the tile) x 32 columns (block mb)
 // read transposed: lane i of a 16-lane group receives column d0 + i of 4 rows
-// per 8-byte load.
+// per 8-byte load; the second load is 4 rows down (K-tile swizzle).
 template <int HD>
 __device__ __forceinline__ bf16x8 read_tr(LdsBytes base, int off, int u) {
   LdsBytes p = base + off + 16 * u * HD * 2;
+  LdsBytes p2 = base + (off ^ kt_xor4<HD>()) + (16 * u + 4) * HD * 2;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p + 4 * HD * 2));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p2);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -85,7 +86,7 @@ struct DqWave {
   int qi, T, lane;
   int ktr[HD / 32];
 
-  // One 64-key tile: K at kb (V swizzle), V at vb (K swizzle), in two halves
+  // One 64-key tile: K at kb (K-tile swizzle), V at vb (K swizzle), in two halves
   // of 32 keys (a half's scores, dP and dS die before the next half starts).
   template <bool MASK>
   __device__ __forceinline__ void tile(LdsBytes kb, LdsBytes vb, int k0) {
@@ -96,7 +97,7 @@ struct DqWave {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int st = 0; st < HD / 16; ++st) {
-        const bf16x8 ak = *reinterpret_cast<const LDS bf16x8*>(kb + v_off<HD>(32 * kb2 + krow, 2 * st + hf));
+        const bf16x8 ak = *reinterpret_cast<const LDS bf16x8*>(kb + kt_off<HD>(32 * kb2 + krow, 2 * st + hf));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[st], s, 0, 0, 0);
         const bf16x8 avv = *reinterpret_cast<const LDS bf16x8*>(vb + k_off<HD>(32 * kb2 + krow, 2 * st + hf));
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avv, df[st], dp, 0, 0, 0);
@@ -137,7 +138,7 @@ template <int HD, bool ALIBI, bool CAUSAL, bool GRAD_BF16>
 __global__ __launch_bounds__(QT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_mfma_kernel(BwdArgs a, DqGrid gm) {
   using C = Cfg<HD>;
-  // two stages (K with the V swizzle, then V with the K swizzle), each its own
+  // two stages (K with the K-tile swizzle, then V with the K swizzle), each its own
   // LDS object so the DMA into one never makes the compiler wait before reads
   // of the other
   __shared__ __attribute__((aligned(16))) unsigned char s0[C::STAGE];
@@ -170,7 +171,7 @@ void bwd_dq_mfma_kernel(BwdArgs a, DqGrid gm) {
   const int q_last = min(a.T, q0 + gm.bm) - 1;
   const int nkt = CAUSAL ? (q_last / BN + 1) : (a.T + BN - 1) / BN;
 
-  Dma<HD, QW, SWZ_V, SWZ_K> dma;
+  Dma<HD, QW, SWZ_KT, SWZ_K> dma;
   dma.init(wave, lane);
   dma.issue(Kg, Vg, 0, a.T, s0, wave);
 
@@ -185,13 +186,26 @@ void bwd_dq_mfma_kernel(BwdArgs a, DqGrid gm) {
   {
     const uint4* qs = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + row * HD);
     const uint4* gs = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.dout) + row * HD);
+    const uint4* os = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.out) + row * HD);
+    // D = <dout, out> of this lane's query: each half of the lane pair (n,
+    // n + 32) holds every other 8-dim chunk of the row
+    float dsum = 0.f;
 #pragma unroll
     for (int s = 0; s < HD / 16; ++s) {
       ws.qf[s] = as_bf16x8(qs[2 * s + hf]);
-      ws.df[s] = as_bf16x8(gs[2 * s + hf]);
+      const uint4 gv = gs[2 * s + hf], ov = os[2 * s + hf];
+      ws.df[s] = as_bf16x8(gv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t gw = comp(gv, e), ow = comp(ov, e);
+        dsum = fmaf(__uint_as_float(gw << 16), __uint_as_float(ow << 16), dsum);
+        dsum = fmaf(__uint_as_float(gw & 0xffff0000u), __uint_as_float(ow & 0xffff0000u), dsum);
+      }
     }
+    ws.Dq = dsum + __shfl_xor(dsum, 32);
     ws.lse2 = a.lse[row] * kLog2eM;
-    ws.Dq = a.D[row];
+    // the dk/dv kernel reads D of every row
+    if (hf == 0 && wave_active && ws.qi < a.T) a.D[row] = ws.Dq;
   }
 #pragma unroll
   for (int mb = 0; mb < HD / 32; ++mb) ws.dq[mb] = f32x16{};

@@ -89,10 +89,35 @@ __host__ __device__ constexpr int q_swz(int r) {
 template <int HD>
 __host__ __device__ constexpr int q_off(int r, int c) { return r * HD * 2 + ((c ^ q_swz<HD>(r)) << 4); }
 
-enum Swz { SWZ_K = 0, SWZ_V = 1, SWZ_Q = 2 };
+// Swizzle of a K tile that the dq backward kernel reads both as 32x32x16
+// A-operand rows (like K in the forward) and transposed (like V in the
+// forward). Row bits 0 and 1 pick the 64-byte quarter (the transposing reads
+// of rows r..r+3 land in different quarters), bits 2 and 3 the chunk inside
+// it (16 rows of a row read spread over all 16 chunks). Measured with
+// SQ_LDS_BANK_CONFLICT on gfx950: zero for both patterns. A lane's second
+// transposing load (4 rows down) sees bit 0 of the swizzle flipped, i.e. its
+// byte offset XOR kt_xor4. The 64-dim tile keeps the V swizzle.
+template <int HD>
+__host__ __device__ constexpr int kt_swz(int r) {
+  return HD == 128 ? (((r >> 2) & 1) | (((r >> 3) & 1) << 1) | ((r & 1) << 2) | (((r >> 1) & 1) << 3)) : v_swz<HD>(r);
+}
+template <int HD>
+__host__ __device__ constexpr int kt_off(int r, int c) { return r * HD * 2 + ((c ^ kt_swz<HD>(r)) << 4); }
+template <int HD>
+constexpr int kt_xor4() { return HD == 128 ? 16 : 0; }
+template <int HD>
+constexpr bool kt_rows_xor4() {
+  for (int r = 0; r < 60; ++r)
+    for (int c = 0; c < HD / 8; ++c)
+      if ((r & 4) == 0 && kt_off<HD>(r + 4, c) != (kt_off<HD>(r, c) ^ kt_xor4<HD>()) + 4 * HD * 2) return false;
+  return true;
+}
+static_assert(kt_rows_xor4<64>() && kt_rows_xor4<128>(), "K-tile swizzle: 4 rows down is XOR kt_xor4 plus 4 rows");
+
+enum Swz { SWZ_K = 0, SWZ_V = 1, SWZ_Q = 2, SWZ_KT = 3 };
 template <int HD, int KIND>
 __host__ __device__ constexpr int swz(int r) {
-  return KIND == SWZ_K ? k_swz<HD>(r) : (KIND == SWZ_V ? v_swz<HD>(r) : q_swz<HD>(r));
+  return KIND == SWZ_K ? k_swz<HD>(r) : (KIND == SWZ_V ? v_swz<HD>(r) : (KIND == SWZ_Q ? q_swz<HD>(r) : kt_swz<HD>(r)));
 }
 
 // Direct global -> LDS staging of one 64-row tile of two tensors (K/V, or Q'/dO
