@@ -105,7 +105,10 @@ def traffic_for(kernel, sources, workload):
     return ent.get("bytes_per_launch")
 
 
-PREFILL_SOURCES = ["transformer_attention_02_amd/csrc/prefill_mfma.hip", "transformer_attention_02_amd/csrc/attn_internal.h"]
+PREFILL_SOURCES = ["transformer_attention_02_amd/csrc/prefill_mfma.hip", "transformer_attention_02_amd/csrc/mfma_tile.h",
+                   "transformer_attention_02_amd/csrc/attn_internal.h"]
+BACKWARD_SOURCES = ["transformer_attention_02_amd/csrc/backward_mfma.hip", "transformer_attention_02_amd/csrc/mfma_tile.h",
+                    "transformer_attention_02_amd/csrc/attn_internal.h"]
 DECODE_SOURCES = ["transformer_attention_02_amd/csrc/decode.hip", "transformer_attention_02_amd/csrc/attn_internal.h"]
 
 
@@ -425,7 +428,8 @@ def main():
                            "kernels_ms": bk}
         cfg["backward"]["kernels_ms_median"], cfg["backward"]["kernels_ms_min"] = med_min("bk")
         line["roofline"] = {"bound": "mfma", "achieved": kt, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": kt / PEAK_BF16_TFLOPS, "traffic": None,
+                            "frac": kt / PEAK_BF16_TFLOPS,
+                            "traffic": traffic_for("backward_mfma", BACKWARD_SOURCES, cfg["workload"]),
                             "kernel": f"bwd_dq_mfma_kernel<{w.hd}> + bwd_dkv_mfma_kernel<{w.hd}> (timed together)"}
     line["config"] = cfg
     torch.cuda.synchronize()
