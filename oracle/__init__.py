@@ -12,3 +12,4 @@ from .attention import (  # noqa: F401
     prefill_flops,
     rope_inv_freq,
 )
+from .fp8 import E4M3_MAX, attention_decode_fp8, e4m3_decode, e4m3_encode, e4m3_values  # noqa: F401
