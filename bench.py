@@ -16,13 +16,17 @@ kernel on its own stream; ``decode.roofline`` is the same for the split-KV
 kernel. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
 same workload.
 
+``--workload decode-fp8`` times attn_decode_fp8_fwd on the same decode step over
+an fp8 (OCP E4M3) cache, with the bf16-cache step in the same run for the
+before/after comparison; ``value`` = fp8 KV bytes read per second.
+
 ``--workload backward`` times attn_prefill_bwd on the Llama-3-8B prefill
 instead (bf16 gradients; ``value`` = backward TFLOP/s with the algorithmic
 10*B*H*hd*T(T+1)/2 flops; ``roofline`` covers its two matrix-core kernels,
 dq and dk/dv, timed together).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload all|prefill|decode|alibi|small|window|chunk|backward|copy]
+                       [--workload all|prefill|decode|decode-fp8|alibi|small|window|chunk|backward|copy]
                        [--no-cpu-baseline] [--no-ceilings]
 """
 from __future__ import annotations
@@ -172,6 +176,22 @@ class Decode:
         return self.w.kv_read_bytes()
 
 
+class DecodeFp8(Decode):
+    """attn_decode_fp8_fwd over uint8 E4M3 caches (same shapes as Decode)."""
+
+    def __call__(self, stream, events=None):
+        w, bd = self.w, self.bd
+        if events:
+            bd.attn_set_timing_events(*events)
+        st = bd.attn_decode_fp8_fwd(self.q.data_ptr(), self.kn.data_ptr(), self.vn.data_ptr(), self.kc.data_ptr(),
+                                    self.vc.data_ptr(), self.lens.data_ptr(), self.out.data_ptr(),
+                                    self.lse.data_ptr(), w.B, w.H, w.KV, w.hd, self.Lmax, w.rope_base, w.alibi,
+                                    w.k_scale, w.v_scale, bd.ATTN_DTYPE_BF16, bd.ATTN_DTYPE_BF16, self.ws.data_ptr(),
+                                    self.ws_bytes, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_decode_fp8_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+
 class Backward:
     """attn_prefill_bwd on the forward's own out/lse (computed once, untimed)."""
 
@@ -252,6 +272,34 @@ def cpu_baseline_leg(pre, dec, heads, seqs):
     return res
 
 
+def cpu_baseline_fp8(dec8, seqs):
+    """The fp64 oracle of the fp8-cache decode step, one sequence at a time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_decode_fp8
+
+    w, inp = dec8.w, dec8.inp
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    pick = list(range(min(seqs, w.B)))
+    t_total, nbytes, errs = 0.0, 0, []
+    for b in pick:
+        L = int(inp.lens[b])
+        kc = dec8.kc[b:b + 1, :, :L].cpu().numpy()
+        vc = dec8.vc[b:b + 1, :, :L].cpu().numpy()
+        t0 = time.perf_counter()
+        ref = attention_decode_fp8(f64(dec8.q[b:b + 1]), f64(dec8.kn[b:b + 1]), f64(dec8.vn[b:b + 1]), kc, vc,
+                                   np.array([L], dtype=np.int32), w.k_scale, w.v_scale, rope_base=w.rope_base,
+                                   alibi=w.alibi)[0]
+        t_total += time.perf_counter() - t0
+        nbytes += (L + 1) * w.KV * w.hd * 2
+        errs.append(float(np.abs(f64(dec8.out[b:b + 1]) - ref).max()))
+    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": nbytes / t_total / 1e9,
+            "unit": "GB/s", "seconds": t_total, "sample": f"sequences 0..{len(pick) - 1} of {w.B}",
+            "max_abs_err_vs_gpu_bf16_out": max(errs)}
+
+
 def cpu_baseline_bwd(bwd, heads):
     """The fp64 oracle backward on a bounded sample: the first ``heads`` query
     heads (whole GQA groups) of batch 0, all rows."""
@@ -285,7 +333,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "alibi", "small", "window", "chunk", "backward", "copy"],
+                    choices=["all", "prefill", "decode", "decode-fp8", "alibi", "small", "window", "chunk", "backward",
+                             "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -333,7 +382,8 @@ def main():
     pre_w = {"all": W.LLAMA3_8B, "prefill": W.LLAMA3_8B, "alibi": W.ALIBI_MHA, "small": W.SMALL_BF16,
              "window": W.LLAMA3_WINDOW, "chunk": W.LLAMA3_CHUNK}.get(args.workload)
     pre = Prefill(pre_w, dev, bd, W, torch) if pre_w is not None else None
-    dec = Decode(W.KV_DECODE, dev, bd, W, torch) if args.workload in ("all", "decode") else None
+    dec = Decode(W.KV_DECODE, dev, bd, W, torch) if args.workload in ("all", "decode", "decode-fp8") else None
+    dec8 = DecodeFp8(W.KV_DECODE_FP8, dev, bd, W, torch) if args.workload == "decode-fp8" else None
     stream = torch.cuda.current_stream().cuda_stream
     bwd = Backward(W.LLAMA3_8B, dev, bd, W, torch, stream) if args.workload == "backward" else None
     log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None} "
@@ -346,10 +396,12 @@ def main():
             dec(stream)
         if bwd:
             bwd(stream)
+        if dec8:
+            dec8(stream)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk")}
+    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk", "ec", "ek")}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
@@ -362,6 +414,10 @@ def main():
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][0]), ctypes.c_void_p(stream))
             dec(stream, ev["dk"][i])
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][1]), ctypes.c_void_p(stream))
+        if dec8:
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["ec"][i][0]), ctypes.c_void_p(stream))
+            dec8(stream, ev["ek"][i])
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["ec"][i][1]), ctypes.c_void_p(stream))
         if bwd:
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["bc"][i][0]), ctypes.c_void_p(stream))
             bwd(stream, ev["bk"][i])
@@ -416,6 +472,26 @@ def main():
             cfg["workload"] = w.name
         else:
             cfg["workload"] = cfg["workload"] + " + " + w.name
+    if dec8:
+        w = dec8.w
+        ec, ek = avg("ec"), avg("ek")
+        gbs = w.kv_read_bytes() / (ec * 1e-3) / 1e9
+        kg = w.kv_read_bytes() / (ek * 1e-3) / 1e9
+        bf = line.pop("decode")
+        line.update(value=gbs, unit="GB/s", metric="fp8 E4M3 KV-cache decode: KV-read GB/s, 1 GPU")
+        line["roofline"] = {"bound": "hbm", "achieved": kg, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": kg / PEAK_HBM_GBS,
+                            "traffic": traffic_for("decode_split_fp8", DECODE_SOURCES, w.name),
+                            "kernel": f"decode_split_mfma_kernel<{w.hd}, fp8>"}
+        cfg["workload"] = w.name
+        cfg["decode_fp8"] = {"B": w.B, "H": w.H, "KV": w.KV, "hd": w.hd, "k_scale": w.k_scale, "v_scale": w.v_scale,
+                             "kv_bytes": w.kv_read_bytes(), "call_ms": ec, "kernel_ms": ek,
+                             "tokens_per_s": w.B / (ec * 1e-3)}
+        cfg["decode_fp8"]["kernel_ms_median"], cfg["decode_fp8"]["kernel_ms_min"] = med_min("ek")
+        # before / after: the bf16-cache step of the same shape in the same run
+        cfg["bf16_cache"] = {"call_ms": bf["call_ms"], "kernel_ms": bf["kernel_ms"], "GB/s": bf["value"],
+                             "kv_bytes": bf["kv_bytes"], "tokens_per_s": W.KV_DECODE.B / (bf["call_ms"] * 1e-3)}
+        line["speedup_vs_bf16_cache"] = bf["call_ms"] / ec
     if bwd:
         w = bwd.w
         bc, bk = avg("bc"), avg("bk")
@@ -438,6 +514,8 @@ def main():
         ok &= bool(torch.isfinite(pre.out).all().item())
     if dec:
         ok &= bool(torch.isfinite(dec.out).all().item())
+    if dec8:
+        ok &= bool(torch.isfinite(dec8.out).all().item())
     if bwd:
         for t in (bwd.dq, bwd.dk, bwd.dv):
             ok &= bool(torch.isfinite(t).all().item())
@@ -467,7 +545,10 @@ def main():
                                      "prefill_kernel_vs_gemm": line["roofline"]["achieved"] / gemm}
         del a_, b_, c_
 
-    if not args.no_cpu_baseline and bwd:
+    if not args.no_cpu_baseline and dec8:
+        log("cpu baseline: timing the fp64 oracle fp8 decode on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_fp8(dec8, args.cpu_seqs)
+    elif not args.no_cpu_baseline and bwd:
         log("cpu baseline: timing the fp64 oracle backward on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline_bwd(bwd, args.cpu_heads_bwd)
     elif not args.no_cpu_baseline:

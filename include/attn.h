@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -74,11 +74,11 @@ const char* attn_last_error(void);
 
 /*
  * Timing hook for benchmarks and profilers. `start` and `stop` are hipEvent_t
- * handles created by the caller (or NULL to clear). The next attn_prefill_fwd
- * or attn_decode_fwd call made by the same thread records `start` on its
- * stream immediately before launching its main kernel (the attention kernel of
- * prefill, the split-KV kernel of decode) and `stop` immediately after it, then
- * clears the hook. The events stay owned by the caller. Always returns ATTN_OK.
+ * handles created by the caller (or NULL to clear). The next prefill, decode
+ * or backward call made by the same thread records `start` on its stream
+ * immediately before launching its main kernel (the attention kernel of
+ * prefill, the split-KV kernel of decode, the dq and dk/dv kernels of the
+ * backward) and `stop` immediately after it, then clears the hook. The events stay owned by the caller. Always returns ATTN_OK.
  */
 int attn_set_timing_events(void* start, void* stop);
 
@@ -225,6 +225,34 @@ int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k
                     const int32_t* cache_lens, void* out, float* lse,
                     int B, int H, int KV, int hd, int Lmax, double rope_base, int alibi,
                     int dtype, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same decode step over a cache held in 8-bit floats, the quantized
+ * storage that "Build a Transformer Self-Attention Block from Scratch in Pure
+ * Python" lists on its roadmap against the memory-bandwidth bottleneck (the
+ * pages fix no format). Each cache element is an OCP FP8 E4M3 code (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; subnormals; no infinities;
+ * largest finite magnitude 448) standing for code_value * scale, with one
+ * scale for all of K and one for all of V.
+ *
+ *   k_cache, v_cache  [B, KV, Lmax, hd] uint8 E4M3 codes: rotated keys / values
+ *                     at slots 0..L-1 (read); slot L receives the codes of
+ *                     R(L) k_new / k_scale and v_new / v_scale (written): the
+ *                     value is clamped to +-448 and rounded to nearest, ties to
+ *                     even mantissa, sign bit copied.
+ *   k_scale, v_scale  positive finite fp32 scales.
+ *   q, k_new, v_new   bf16 (dtype must be ATTN_DTYPE_BF16); every other
+ *                     argument as for attn_decode_fwd (same workspace size).
+ * The query attends slots 0..L of the dequantized cache, the new slot as
+ * stored. Supported: hd in {64, 128}, H / KV <= 16 (ATTN_ERR_UNSUPPORTED
+ * otherwise; ATTN_ERR_SHAPE for a non-positive or non-finite scale). Traffic
+ * per step is half that of a bf16 cache.
+ */
+int attn_decode_fp8_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* cache_lens, void* out, float* lse,
+                        int B, int H, int KV, int hd, int Lmax, double rope_base, int alibi,
+                        float k_scale, float v_scale, int dtype, int out_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

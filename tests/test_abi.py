@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bd.attn_abi_version() == 2
+    assert bd.attn_abi_version() == 3
     names = {c: bd.attn_status_str(c) for c in range(7)}
     assert names == {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
                      4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP"}
@@ -188,6 +188,31 @@ def test_decode_validation(kw, code):
     assert st == code, (st, bd.attn_last_error())
 
 
+def _decode_fp8(**kw):
+    args = dict(q=FAKE, k_new=FAKE2, v_new=FAKE3, k_cache=FAKE4, v_cache=0x50000, cache_lens=0x60000,
+                out=0x70000, lse=None, B=2, H=8, KV=2, hd=128, Lmax=1000, rope_base=10000.0, alibi=0,
+                k_scale=1 / 64, v_scale=1 / 64, dtype=bd.ATTN_DTYPE_BF16, out_dtype=bd.ATTN_DTYPE_F32,
+                workspace=0x100000, workspace_bytes=1 << 24, stream=None)
+    args.update(kw)
+    return bd.attn_decode_fp8_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v_cache=None), bd.ATTN_ERR_NULL),
+    (dict(k_scale=0.0), bd.ATTN_ERR_SHAPE),
+    (dict(v_scale=-1.0), bd.ATTN_ERR_SHAPE),
+    (dict(k_scale=float("inf")), bd.ATTN_ERR_SHAPE),
+    (dict(v_scale=float("nan")), bd.ATTN_ERR_SHAPE),
+    (dict(dtype=bd.ATTN_DTYPE_F32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(hd=32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(H=34, KV=2), bd.ATTN_ERR_UNSUPPORTED),   # 17 query heads per KV head
+    (dict(workspace_bytes=64), bd.ATTN_ERR_WORKSPACE),
+])
+def test_decode_fp8_validation(kw, code):
+    st = _decode_fp8(**kw)
+    assert st == code, (st, bd.attn_last_error())
+
+
 def test_decode_workspace_size():
     n = bd.attn_decode_workspace_bytes(64, 32, 8, 128, 8193)
     nsplit = -(-8193 // 256)
@@ -207,3 +232,4 @@ def test_launch_without_a_device_reports_hip_error():
     st = _prefill()
     assert st == bd.ATTN_ERR_HIP
     assert "launch" in bd.attn_last_error()
+    assert _decode_fp8() == bd.ATTN_ERR_HIP

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_decode, attention_prefill, attention_prefill_bwd
+from oracle import attention_decode, attention_decode_fp8, attention_prefill, attention_prefill_bwd, e4m3_decode
 from transformer_attention_02_amd import binding as bd
 from transformer_attention_02_amd import workloads as W
 
@@ -408,6 +408,97 @@ def test_decode_long_split_path():
     for i, b in enumerate(pick):
         L = int(lens[b])
         assert np.array_equal(to64(vc[b, :, L]), vs[i])
+
+
+# ------------------------------------------------------------- fp8 decode
+def gpu_decode_fp8(inp: W.DecodeInputs, w: W.DecodeWorkload, alibi=0, out_dtype=torch.float32):
+    lens = torch.from_numpy(inp.lens).cuda()
+    kc, vc = inp.k_cache.cuda(), inp.v_cache.cuda()
+    B, H, hd = inp.q.shape
+    out = torch.full((B, H, hd), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+    bd.decode_fp8(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda(), kc, vc, lens, w.k_scale, w.v_scale,
+                  rope_base=w.rope_base, alibi=alibi, out=out, lse=lse, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, lse, kc.cpu(), vc.cpu()
+
+
+def check_slot_codes(got, ref, pre):
+    """Written E4M3 codes: equal to the oracle's, except where the value sits on a
+    rounding tie to within the kernel's fp32 arithmetic (the oracle rounds the fp64
+    value, the kernel its fp32 value); there the other neighbour is accepted."""
+    got, ref = np.asarray(got, dtype=np.uint8), np.asarray(ref, dtype=np.uint8)
+    bad = np.nonzero(got != ref)
+    dg = np.abs(e4m3_decode(got[bad]) - pre[bad])
+    dr = np.abs(e4m3_decode(ref[bad]) - pre[bad])
+    assert np.all(dg - dr <= 1e-6 * np.maximum(np.abs(pre[bad]), 1.0)), (got[bad], ref[bad], pre[bad])
+    return len(bad[0])
+
+
+@pytest.mark.parametrize("hd,H,KV", [(128, 8, 2), (64, 16, 4), (128, 16, 1)])
+@pytest.mark.parametrize("alibi", [0, 1])
+def test_decode_fp8_ragged_lengths(hd, H, KV, alibi):
+    w = W.DecodeWorkload("decode-fp8-small", 6, H, KV, hd, 0, 0, 5, 51, 10000.0, cache="fp8", k_scale=1 / 64,
+                         v_scale=1 / 48)
+    lens = np.array([0, 1, 255, 256, 257, 700], dtype=np.int32)
+    inp = W.decode_inputs(w, lens=lens, lmax=702)
+    print(f"[decode fp8] hd={hd} H={H} KV={KV} alibi={alibi} lens={lens.tolist()}", flush=True)
+    out, lse, kc, vc = gpu_decode_fp8(inp, w, alibi)
+    ref, ref_lse, ks, vs, kp, vp = attention_decode_fp8(to64(inp.q), to64(inp.k_new), to64(inp.v_new),
+                                                        inp.k_cache.numpy(), inp.v_cache.numpy(), lens, w.k_scale,
+                                                        w.v_scale, rope_base=w.rope_base, alibi=alibi)
+    err = np.abs(to64(out) - ref).max()
+    print(f"  max abs err {err:.3g}", flush=True)
+    assert err <= 1e-2
+    assert np.abs(to64(lse) - ref_lse).max() <= 2e-2
+    kc_np, vc_np, k0, v0 = kc.numpy(), vc.numpy(), inp.k_cache.numpy(), inp.v_cache.numpy()
+    ties = 0
+    for b, L in enumerate(lens):
+        ties += check_slot_codes(kc_np[b, :, L], ks[b], kp[b])
+        ties += check_slot_codes(vc_np[b, :, L], vs[b], vp[b])
+        assert np.array_equal(kc_np[b, :, :L], k0[b, :, :L]) and np.array_equal(vc_np[b, :, :L], v0[b, :, :L])
+        assert np.array_equal(kc_np[b, :, L + 1:], k0[b, :, L + 1:])
+    print(f"  slot codes differing on a tie: {ties}", flush=True)
+
+
+def test_decode_fp8_full_size_sampled():
+    w = W.KV_DECODE_FP8
+    print(f"[full-size decode fp8] {w.name}", flush=True)
+    inp = W.decode_inputs(w)
+    out, lse, kc, vc = gpu_decode_fp8(inp, w, out_dtype=torch.bfloat16)
+    assert torch.isfinite(out).all().item()
+    lens = inp.lens
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63})
+    ref, ref_lse, ks, vs, kp, vp = attention_decode_fp8(
+        to64(inp.q[pick]), to64(inp.k_new[pick]), to64(inp.v_new[pick]), inp.k_cache[pick].numpy(),
+        inp.v_cache[pick].numpy(), lens[pick], w.k_scale, w.v_scale, rope_base=w.rope_base)
+    err = np.abs(to64(out[pick]) - ref).max()
+    print(f"  max abs err {err:.3g} (bf16 output)", flush=True)
+    assert err <= 1e-2
+    assert np.abs(to64(lse[pick]) - ref_lse).max() <= 2e-2
+    for i, b in enumerate(pick):
+        L = int(lens[b])
+        check_slot_codes(kc[b, :, L].numpy(), ks[i], kp[i])
+        check_slot_codes(vc[b, :, L].numpy(), vs[i], vp[i])
+
+
+def test_decode_fp8_matches_bf16_decode_of_the_dequantized_cache():
+    """The fp8 step equals (to accumulation order) the bf16 step over a cache holding
+    the dequantized values when the new token's key and value are already on the
+    grid: the scales fold into the scores and the output exactly."""
+    w = W.DecodeWorkload("decode-fp8-vs-bf16", 4, 8, 2, 128, 0, 0, 5, 61, 0.0, cache="fp8", k_scale=1 / 64,
+                         v_scale=1 / 64)
+    lens = np.array([3, 100, 513, 1000], dtype=np.int32)
+    inp = W.decode_inputs(w, lens=lens, lmax=1001)
+    # new K/V on the grid: quantize-dequantize them first (no rotation: rope_base 0)
+    kn = (W.to_e4m3_codes(inp.k_new, w.k_scale).view(torch.float8_e4m3fn).float() * w.k_scale).to(torch.bfloat16)
+    vn = (W.to_e4m3_codes(inp.v_new, w.v_scale).view(torch.float8_e4m3fn).float() * w.v_scale).to(torch.bfloat16)
+    inp8 = W.DecodeInputs(inp.q, kn, vn, inp.k_cache, inp.v_cache, lens)
+    out8, lse8, _, _ = gpu_decode_fp8(inp8, w)
+    kd = (inp.k_cache.view(torch.float8_e4m3fn).float() * w.k_scale).to(torch.bfloat16)
+    vd = (inp.v_cache.view(torch.float8_e4m3fn).float() * w.v_scale).to(torch.bfloat16)
+    out16, lse16, _, _ = gpu_decode(W.DecodeInputs(inp.q, kn, vn, kd, vd, lens), 0.0)
+    assert torch.allclose(out8, out16, rtol=0, atol=2e-3) and torch.allclose(lse8, lse16, rtol=0, atol=2e-3)
 
 
 def test_incremental_decode_equals_prefill():

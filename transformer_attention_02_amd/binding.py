@@ -44,12 +44,14 @@ EXPORTS = (
     "attn_prefill_bwd",
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
+    "attn_decode_fp8_fwd",
 )
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _D = ctypes.c_double
 _S = ctypes.c_size_t
+_F = ctypes.c_float
 
 _SIGS = {
     "attn_abi_version": (_I, []),
@@ -65,6 +67,8 @@ _SIGS = {
                               _S, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I, _P, _S, _P]),
+    "attn_decode_fp8_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _F, _F, _I, _I, _P, _S,
+                                 _P]),
 }
 
 _lib = None
@@ -148,6 +152,13 @@ def attn_decode_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, 
                     dtype, out_dtype, workspace, workspace_bytes, stream) -> int:
     return load().attn_decode_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax,
                                   float(rope_base), alibi, dtype, out_dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_fp8_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base, alibi,
+                        k_scale, v_scale, dtype, out_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().attn_decode_fp8_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax,
+                                      float(rope_base), alibi, float(k_scale), float(v_scale), dtype, out_dtype,
+                                      workspace, workspace_bytes, stream)
 
 
 # --------------------------------------------------------------- torch helpers
@@ -274,5 +285,32 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_lens, *, rope_base=10000.0, 
                          cache_lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
                          B, H, KV, hd, Lmax, rope_base, alibi, dt, _dtype_code(out), workspace.data_ptr(), nbytes,
                          _stream_ptr(stream))
+    _check(st)
+    return out, lse
+
+
+def decode_fp8(q, k_new, v_new, k_cache, v_cache, cache_lens, k_scale, v_scale, *, rope_base=10000.0,
+               alibi=ATTN_ALIBI_NONE, out_dtype=None, want_lse=True, out=None, lse=None, workspace=None, stream=None):
+    """Run attn_decode_fp8_fwd: caches are uint8 tensors of E4M3 codes. Returns (out, lse)."""
+    import torch
+
+    B, H, hd = q.shape
+    KV, Lmax = k_cache.shape[1], k_cache.shape[2]
+    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
+    assert k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(B, H, hd, dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace, nbytes = decode_workspace(B, H, KV, hd, Lmax, q.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    st = attn_decode_fp8_fwd(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                             v_cache.data_ptr(), cache_lens.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, B, H, KV, hd, Lmax, rope_base, alibi,
+                             k_scale, v_scale, _dtype_code(q), _dtype_code(out), workspace.data_ptr(), nbytes,
+                             _stream_ptr(stream))
     _check(st)
     return out, lse

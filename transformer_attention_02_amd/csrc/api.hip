@@ -2,6 +2,8 @@
 // Every check runs before the first HIP call; nothing here allocates, frees or
 // synchronises.
 #include <math.h>
+
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -353,10 +355,11 @@ size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax) {
   return (size_t)decode_ws_layout(B, H, hd, Lmax).total;
 }
 
-int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                    const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
-                    double rope_base, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+namespace {
+int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
+                double rope_base, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                void* stream, int fp8, float k_scale, float v_scale) {
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !out)
     return fail(ATTN_ERR_NULL, "q, k_new, v_new, k_cache, v_cache, cache_lens and out must be non-NULL");
   if (B <= 0 || H <= 0 || KV <= 0 || Lmax <= 0)
@@ -402,9 +405,37 @@ int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k
   a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
   a.freqs = make_freqs(hd, rope_base);
+  a.fp8 = fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  if (fp8) {
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+      return fail(ATTN_ERR_SHAPE, "k_scale and v_scale must be positive and finite (%g, %g)", (double)k_scale,
+                  (double)v_scale);
+    if (dtype != ATTN_DTYPE_BF16 || !decode_mfma_supported(a, 1))
+      return fail(ATTN_ERR_UNSUPPORTED, "fp8 cache: bf16 q/k_new/v_new, hd 64 or 128 and H/KV <= 16 (got dtype %d, "
+                                        "hd %d, H/KV %d)", dtype, hd, H / KV);
+  }
   const TimingHook tm = take_timing();
   return hip_status(launch_decode(a, dtype == ATTN_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream), tm),
                     "decode launch");
+}
+}  // namespace
+
+int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
+                    double rope_base, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_impl(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base, alibi,
+                     dtype, out_dtype, workspace, workspace_bytes, stream, 0, 1.f, 1.f);
+}
+
+int attn_decode_fp8_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
+                        double rope_base, int alibi, float k_scale, float v_scale, int dtype, int out_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base, alibi,
+                     dtype, out_dtype, workspace, workspace_bytes, stream, 1, k_scale, v_scale);
 }
 
 }  // extern "C"

@@ -12,6 +12,7 @@ constexpr int kMaxHeadDim = 128;
 constexpr int kDecodeSplit = 256;  // keys per split-KV partial, vector-ALU decode kernel
 constexpr int kSplitMfma = 512;    // keys per split-KV partial, MFMA decode kernel
 constexpr int kSplitMfmaLong = 1024;  // the same when the batch gives enough splits anyway
+constexpr int kSplitMfmaFp8 = 2048;   // fp8 cache: the same bytes per workgroup as the long bf16 split
 
 // 4 theta_i / (2 pi) in fp64 (quarter turns per position) for i = 0 .. hd/2-1,
 // theta_i = base^(-2i/hd).
@@ -65,6 +66,8 @@ struct DecodeArgs {
   int out_bf16;
   float scale_log2;
   RopeFreqs freqs;
+  int fp8;               // caches hold OCP E4M3 codes (value = code * scale)
+  float k_scale, v_scale;
 };
 
 struct BwdArgs {
@@ -112,6 +115,7 @@ hipError_t launch_prefill_valu(const PrefillArgs& a, int bf16, hipStream_t s);
 bool prefill_mfma_supported(const PrefillArgs& a, int bf16);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s, const TimingHook& tm);
+bool decode_mfma_supported(const DecodeArgs& a, int bf16);
 hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t s);
 hipError_t launch_bwd_valu(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkv_valu(const BwdArgs& a, hipStream_t s);

@@ -169,13 +169,44 @@ __device__ __forceinline__ int dv_off(int r, int c) {  // V tile: 16-byte chunk 
   }
 }
 
-template <int HD, int TPW>
+// fp8 cache: OCP E4M3 code of x (x already divided by the scale): |x| clamped
+// to 448 and rounded to nearest, ties to even mantissa; subnormals below 2^-6
+// are multiples of 2^-9; the sign bit is x's.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sgn = (bits >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  if (a < 0.015625f) return sgn | (uint32_t)rintf(a * 512.f);  // 0..8 (8 is the smallest normal)
+  const uint32_t ab = __float_as_uint(a);
+  int e = (int)(ab >> 23) - 127;
+  uint32_t m = (ab >> 20) & 7u;
+  const uint32_t rem = ab & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+  if (m == 8u) {
+    m = 0u;
+    ++e;
+  }
+  return sgn | ((uint32_t)(e + 7) << 3) | m;
+}
+
+// Four E4M3 codes (one 32-bit word) -> four bf16 (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+template <int HD, int TPW, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int SPLIT = kWaves * kTile * TPW;  // key slots per workgroup
-  constexpr int KCH = HD / 8;                 // 16-byte chunks per row
-  constexpr int TILE_BYTES = kTile * HD * 2;  // one K or V tile
-  constexpr int LOADS = kTile * KCH / 64;     // 16-byte loads per lane per tensor
+  constexpr int KCH = HD / 8;                 // 16-byte bf16 chunks per row (in LDS)
+  constexpr int EB = FP8 ? 1 : 2;             // cache bytes per element
+  constexpr int GCH = HD * EB / 16;           // 16-byte chunks per cache row (in memory)
+  constexpr int TILE_BYTES = kTile * HD * 2;  // one K or V tile in LDS (bf16)
+  constexpr int LOADS = kTile * GCH / 64;     // 16-byte loads per lane per tensor
+  constexpr int NSLOT = FP8 ? 4 : 2;          // tiles in flight per wave (about the same bytes either way)
   __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * 2 * TILE_BYTES];
   __shared__ float mer_m[kWaves][16];
   __shared__ float mer_l[kWaves][16];
@@ -189,29 +220,36 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   const int nk = L + 1;
   const int k0 = sp * SPLIT;
   if (k0 >= nk) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index read from lane 0, so the compiler knows it is wave-uniform:
+  // the buffer descriptors built from it stay scalar (no per-load waterfall loop)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
   const int G = a.group;
   const bool qcol = n < G;
   const int head = kvh * G + (qcol ? n : 0);
 
-  const long cbase = ((long)b * a.KV + kvh) * (long)a.Lmax * HD;
-  const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k_cache) + cbase;
-  const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v_cache) + cbase;
+  const long cbase = ((long)b * a.KV + kvh) * (long)a.Lmax * HD;  // elements
+  const unsigned char* Kg = reinterpret_cast<const unsigned char*>(a.k_cache) + cbase * EB;
+  const unsigned char* Vg = reinterpret_cast<const unsigned char*>(a.v_cache) + cbase * EB;
   unsigned char* kl = smem + wave * 2 * TILE_BYTES;
   unsigned char* vl = kl + TILE_BYTES;
 
-  // Two tiles of K/V in flight per wave: slot t&1 holds tile t until it is
-  // written to LDS, then receives tile t+2. The first two go out before the
-  // rotary table and the query set-up, which then hide under their latency.
+  // NSLOT tiles of K/V in flight per wave: slot t % NSLOT holds tile t until it
+  // is written to LDS, then receives tile t + NSLOT. The first ones go out
+  // before the rotary table and the query set-up, which then hide under their
+  // latency.
   // Buffer descriptors start at the tile and end at key slot nk, so rows past
   // the sequence end read as zero. (The wave whose tile covers slot L may read
   // it before the new key lands there; it patches that row in LDS.)
-  uint4 kr[2][LOADS], vr[2][LOADS];
+  uint4 kr[NSLOT][LOADS], vr[NSLOT][LOADS];
+  // Issued unconditionally (a tile at or past the sequence end gets an empty
+  // descriptor: every lane reads zero and no memory is touched), so the wait
+  // before each tile's LDS write counts only that tile's loads; a conditional
+  // issue would make the compiler drain every load in flight there.
   auto load_tile = [&](int slot, int ts) {
-    const int bytes = (nk - ts) * HD * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)ts * HD, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)ts * HD, bytes);
+    const int bytes = max(nk - ts, 0) * HD * EB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)ts * HD * EB, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)ts * HD * EB, bytes);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       kr[slot][i] = buffer_load16_stream(rk, 16 * (lane + 64 * i));
@@ -219,8 +257,9 @@ void decode_split_mfma_kernel(DecodeArgs a) {
     }
   };
   const auto tile_start = [&](int t) { return k0 + (t * kWaves + wave) * kTile; };
-  if (tile_start(0) < nk) load_tile(0, tile_start(0));
-  if (TPW > 1 && tile_start(1) < nk) load_tile(1, tile_start(1));
+#pragma unroll
+  for (int t = 0; t < NSLOT; ++t)
+    if (t < TPW) load_tile(t, tile_start(t));
 
   // cos/sin of the rotary angle at position L for every pair, shared in LDS.
   __shared__ float2 cs_tab[HD / 2];
@@ -233,19 +272,34 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   // key and the value to the cache, and the wave whose tile covers slot L
   // patches that row of its LDS tile (it never reads slot L back from memory).
   const bool own_slot = L >= k0 && L < k0 + SPLIT;
-  uint32_t knew = 0, vnew = 0;  // lane p < HD/2: pair p of R(L) k_new and v_new (bf16x2)
+  uint32_t knew = 0, vnew = 0;  // lane p < HD/2: pair p of R(L) k_new and v_new (bf16x2, as read back)
   const long cslot = (((long)b * a.KV + kvh) * a.Lmax + L) * HD;
   const long nslot = ((long)b * a.KV + kvh) * HD;
   __syncthreads();
   if (own_slot && lane < HD / 2) {
     const uint32_t kw = reinterpret_cast<const uint32_t*>(a.k_new)[(nslot >> 1) + lane];
-    vnew = reinterpret_cast<const uint32_t*>(a.v_new)[(nslot >> 1) + lane];
+    const uint32_t vw = reinterpret_cast<const uint32_t*>(a.v_new)[(nslot >> 1) + lane];
     const float2 t = cs_tab[lane];
     const float x0 = bf16_bits_to_f32(kw & 0xffffu), x1 = bf16_bits_to_f32(kw >> 16);
-    knew = pack_bf16x2(rot0(x0, x1, t.x, t.y), rot1(x0, x1, t.x, t.y));
-    if (wave == 0) {
-      reinterpret_cast<uint32_t*>(a.k_cache)[(cslot >> 1) + lane] = knew;
-      reinterpret_cast<uint32_t*>(a.v_cache)[(cslot >> 1) + lane] = vnew;
+    const float y0 = rot0(x0, x1, t.x, t.y), y1 = rot1(x0, x1, t.x, t.y);
+    if constexpr (FP8) {
+      // stored as E4M3 codes of value / scale; the LDS patch holds what a read returns
+      const uint32_t kc = e4m3_code(y0 / a.k_scale) | (e4m3_code(y1 / a.k_scale) << 8);
+      const uint32_t vc = e4m3_code(bf16_bits_to_f32(vw & 0xffffu) / a.v_scale) |
+                          (e4m3_code(bf16_bits_to_f32(vw >> 16) / a.v_scale) << 8);
+      knew = e4m3x4_to_bf16(kc).x;
+      vnew = e4m3x4_to_bf16(vc).x;
+      if (wave == 0) {
+        reinterpret_cast<uint16_t*>(a.k_cache)[(cslot >> 1) + lane] = (uint16_t)kc;
+        reinterpret_cast<uint16_t*>(a.v_cache)[(cslot >> 1) + lane] = (uint16_t)vc;
+      }
+    } else {
+      knew = pack_bf16x2(y0, y1);
+      vnew = vw;
+      if (wave == 0) {
+        reinterpret_cast<uint32_t*>(a.k_cache)[(cslot >> 1) + lane] = knew;
+        reinterpret_cast<uint32_t*>(a.v_cache)[(cslot >> 1) + lane] = vnew;
+      }
     }
   }
 
@@ -269,7 +323,7 @@ void decode_split_mfma_kernel(DecodeArgs a) {
       qf[s] = __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
     }
   }
-  const float c2 = a.scale_log2;
+  const float c2 = FP8 ? a.scale_log2 * a.k_scale : a.scale_log2;  // K's scale folds into the scores
   const float slope2 = a.alibi ? alibi_slope(a.alibi, head, a.H) * kLog2e : 0.f;
 
   f32x4_t oacc[HD / 16];
@@ -281,20 +335,32 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   for (int t = 0; t < TPW; ++t) {
     const int ts = tile_start(t);
     if (ts >= nk) break;
-    const int slot = t & 1;
+    const int slot = t % NSLOT;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int e = lane + 64 * i;
-      const int r = e / KCH, c = e % KCH;
-      *reinterpret_cast<uint4*>(kl + dk_off<HD>(r, c)) = kr[slot][i];
-      *reinterpret_cast<uint4*>(vl + dv_off<HD>(r, c)) = vr[slot][i];
+      const int r = e / GCH, c = e % GCH;
+      if constexpr (FP8) {  // 16 codes -> two bf16 chunks 2c, 2c+1 of the row
+        const uint4 kq = kr[slot][i], vq = vr[slot][i];
+        const uint2 k0 = e4m3x4_to_bf16(kq.x), k1 = e4m3x4_to_bf16(kq.y), k2 = e4m3x4_to_bf16(kq.z),
+                    k3 = e4m3x4_to_bf16(kq.w);
+        const uint2 v0 = e4m3x4_to_bf16(vq.x), v1 = e4m3x4_to_bf16(vq.y), v2 = e4m3x4_to_bf16(vq.z),
+                    v3 = e4m3x4_to_bf16(vq.w);
+        *reinterpret_cast<uint4*>(kl + dk_off<HD>(r, 2 * c)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        *reinterpret_cast<uint4*>(kl + dk_off<HD>(r, 2 * c + 1)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
+        *reinterpret_cast<uint4*>(vl + dv_off<HD>(r, 2 * c)) = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        *reinterpret_cast<uint4*>(vl + dv_off<HD>(r, 2 * c + 1)) = make_uint4(v2.x, v2.y, v3.x, v3.y);
+      } else {
+        *reinterpret_cast<uint4*>(kl + dk_off<HD>(r, c)) = kr[slot][i];
+        *reinterpret_cast<uint4*>(vl + dv_off<HD>(r, c)) = vr[slot][i];
+      }
     }
     if (own_slot && L >= ts && L < ts + kTile && lane < HD / 2) {
       const int r = L - ts;  // pair `lane` sits in chunk lane/4, bytes 4*(lane%4)
       *reinterpret_cast<uint32_t*>(kl + dk_off<HD>(r, lane >> 2) + 4 * (lane & 3)) = knew;
       *reinterpret_cast<uint32_t*>(vl + dv_off<HD>(r, lane >> 2) + 4 * (lane & 3)) = vnew;
     }
-    if (t + 2 < TPW && tile_start(t + 2) < nk) load_tile(slot, tile_start(t + 2));
+    if (t + NSLOT < TPW) load_tile(slot, tile_start(t + NSLOT));
 
     // S^T = K Q^T for the tile's two 16-key blocks
     f32x4_t sacc[2];
@@ -380,7 +446,7 @@ void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) o += ob[(w * 16 + col) * HD + d];
     const long pidx = ((long)b * a.H + kvh * G + col) * a.nsplit + sp;
-    a.part_o[pidx * HD + d] = o;
+    a.part_o[pidx * HD + d] = FP8 ? o * a.v_scale : o;  // V's scale, applied once per partial
     if (d == 0) {
       float Mc = -INFINITY;
 #pragma unroll
@@ -461,19 +527,26 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   if (a.lse && lane == 0) a.lse[(long)b * a.H + h] = lse;
 }
 
+}  // namespace
+
 bool decode_mfma_supported(const DecodeArgs& a, int bf16) {
   return bf16 && (a.hd == 64 || a.hd == 128) && a.group <= 16;
 }
+
+namespace {
 
 template <int BF16, int HD>
 hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHook& tm) {
   DecodeArgs a = a0;
   const bool mfma = decode_mfma_supported(a, BF16);
+  if (a.fp8 && !mfma) return hipErrorInvalidValue;  // the host checks this first
   // MFMA path: the longer split when it still gives at least four workgroups
   // per CU (measured on the 64-sequence, 8-KV-head cache: 5.6 -> 6.0 TB/s), so
   // the per-workgroup set-up is amortised over more keys.
   const bool long_split = (long)a.KV * a.B * ((a.Lmax + kSplitMfmaLong - 1) / kSplitMfmaLong) >= 1024;
-  a.split = mfma ? (long_split ? kSplitMfmaLong : kSplitMfma) : kDecodeSplit;
+  // fp8: half the bytes per key, so twice the keys per workgroup for the same set-up cost
+  const bool fp8_split = a.fp8 && (long)a.KV * a.B * ((a.Lmax + kSplitMfmaFp8 - 1) / kSplitMfmaFp8) >= 1024;
+  a.split = mfma ? (fp8_split ? kSplitMfmaFp8 : (long_split ? kSplitMfmaLong : kSplitMfma)) : kDecodeSplit;
   a.nsplit = (a.Lmax + a.split - 1) / a.split;
   hipError_t e = hipSuccess;
   if (!mfma) {  // the MFMA split kernel appends the new token itself
@@ -484,10 +557,19 @@ hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHoo
   if (mfma) {
     if constexpr (HD == 64 || HD == 128) {
       constexpr int TPW = kSplitMfma / (kWaves * kTile);
-      if (a.split == kSplitMfmaLong) {
-        hipLaunchKernelGGL((decode_split_mfma_kernel<HD, 2 * TPW>), dim3(a.KV * a.B, a.nsplit), dim3(256), 0, s, a);
+      const dim3 grid(a.KV * a.B, a.nsplit);
+      if (a.fp8) {
+        if (a.split == kSplitMfmaFp8) {
+          hipLaunchKernelGGL((decode_split_mfma_kernel<HD, 4 * TPW, true>), grid, dim3(256), 0, s, a);
+        } else if (a.split == kSplitMfmaLong) {
+          hipLaunchKernelGGL((decode_split_mfma_kernel<HD, 2 * TPW, true>), grid, dim3(256), 0, s, a);
+        } else {
+          hipLaunchKernelGGL((decode_split_mfma_kernel<HD, TPW, true>), grid, dim3(256), 0, s, a);
+        }
+      } else if (a.split == kSplitMfmaLong) {
+        hipLaunchKernelGGL((decode_split_mfma_kernel<HD, 2 * TPW, false>), grid, dim3(256), 0, s, a);
       } else {
-        hipLaunchKernelGGL((decode_split_mfma_kernel<HD, TPW>), dim3(a.KV * a.B, a.nsplit), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_split_mfma_kernel<HD, TPW, false>), grid, dim3(256), 0, s, a);
       }
     }
   } else {

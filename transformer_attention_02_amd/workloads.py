@@ -89,6 +89,9 @@ class DecodeWorkload:
     rope_base: float
     alibi: int = 0
     dtype: str = BF16
+    cache: str = "same"    # "same": the cache has dtype; "fp8": OCP E4M3 codes with k_scale / v_scale
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     def lengths(self) -> np.ndarray:
         rng = np.random.default_rng(self.len_seed)
@@ -99,7 +102,7 @@ class DecodeWorkload:
 
     def kv_read_bytes(self) -> int:
         """K and V bytes the step must read: (len_b + 1) rows of K and V per KV head."""
-        e = 4 if self.dtype == F32 else 2
+        e = 1 if self.cache == "fp8" else (4 if self.dtype == F32 else 2)
         return int(sum(int(L) + 1 for L in self.lengths()) * self.KV * self.hd * 2 * e)
 
 
@@ -117,6 +120,11 @@ LLAMA3_CHUNK = PrefillWorkload("llama3-8b chunked prefill: tokens 3584..4095 ove
                                4, 4096, 32, 8, 128, BF16, 3, 500000.0, Tq=512, q_offset=3584)
 KV_DECODE = DecodeWorkload("kv-decode B=64 len~U[512,8192] H=32 KV=8 hd=128",
                            64, 32, 8, 128, 512, 8192, 5, 5, 10000.0)
+# the same step over an fp8 cache: the bf16 draws above, stored as E4M3 codes of
+# value * 64 (|N(0,1)| * 64 stays well inside the +-448 range)
+KV_DECODE_FP8 = DecodeWorkload("kv-decode fp8 E4M3 cache (scale 1/64) B=64 len~U[512,8192] H=32 KV=8 hd=128",
+                               64, 32, 8, 128, 512, 8192, 5, 5, 10000.0, cache="fp8", k_scale=1 / 64,
+                               v_scale=1 / 64)
 
 PREFILL_WORKLOADS = {"tiny": TINY_FP32, "small": SMALL_BF16, "llama3": LLAMA3_8B, "alibi": ALIBI_MHA,
                      "window": LLAMA3_WINDOW, "chunk": LLAMA3_CHUNK}
@@ -236,8 +244,22 @@ def decode_inputs(w: DecodeWorkload, *, B: int | None = None, lens: np.ndarray |
     tdt = torch.bfloat16 if w.dtype == BF16 else torch.float32
     k_cache = torch.zeros(B, w.KV, Lmax, w.hd, dtype=tdt, device=device)
     v_cache = torch.zeros(B, w.KV, Lmax, w.hd, dtype=tdt, device=device)
+    if w.cache == "fp8":
+        k_cache = torch.zeros(B, w.KV, Lmax, w.hd, dtype=torch.uint8, device=device)
+        v_cache = torch.zeros(B, w.KV, Lmax, w.hd, dtype=torch.uint8, device=device)
     for b in range(B):
         L = int(lens[b])
-        k_cache[b, :, :L] = draw(g, (w.KV, L, w.hd)).to(device)
-        v_cache[b, :, :L] = draw(g, (w.KV, L, w.hd)).to(device)
+        kx = draw(g, (w.KV, L, w.hd))
+        vx = draw(g, (w.KV, L, w.hd))
+        if w.cache == "fp8":
+            kx, vx = to_e4m3_codes(kx, w.k_scale), to_e4m3_codes(vx, w.v_scale)
+        k_cache[b, :, :L] = kx.to(device)
+        v_cache[b, :, :L] = vx.to(device)
     return DecodeInputs(q, k_new, v_new, k_cache, v_cache, lens)
+
+
+def to_e4m3_codes(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """uint8 OCP E4M3 codes of x / scale by torch's own float8_e4m3fn conversion
+    (round to nearest even), clamped to the finite range first; used only to
+    synthesise fp8 cache contents."""
+    return (x.float() / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
