@@ -20,13 +20,17 @@ same workload.
 an fp8 (OCP E4M3) cache, with the bf16-cache step in the same run for the
 before/after comparison; ``value`` = fp8 KV bytes read per second.
 
+``--workload latent-decode`` times attn_decode_latent_fwd: 64 sequences of the
+same lengths over a cache of one 512-number latent per token (16 heads of 128
+dims up-projected from it); ``value`` = latent bytes read per second.
+
 ``--workload backward`` times attn_prefill_bwd on the Llama-3-8B prefill
 instead (bf16 gradients; ``value`` = backward TFLOP/s with the algorithmic
 10*B*H*hd*T(T+1)/2 flops; ``roofline`` covers its two matrix-core kernels,
 dq and dk/dv, timed together).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload all|prefill|decode|decode-fp8|alibi|small|window|chunk|backward|copy]
+                       [--workload all|prefill|decode|decode-fp8|latent-decode|alibi|small|window|chunk|backward|copy]
                        [--no-cpu-baseline] [--no-ceilings]
 """
 from __future__ import annotations
@@ -111,6 +115,8 @@ def traffic_for(kernel, sources, workload):
 
 PREFILL_SOURCES = ["transformer_attention_02_amd/csrc/prefill_mfma.hip", "transformer_attention_02_amd/csrc/mfma_tile.h",
                    "transformer_attention_02_amd/csrc/attn_internal.h"]
+LATENT_SOURCES = ["transformer_attention_02_amd/csrc/decode_latent.hip", "transformer_attention_02_amd/csrc/mfma_tile.h",
+                  "transformer_attention_02_amd/csrc/attn_internal.h"]
 BACKWARD_SOURCES = ["transformer_attention_02_amd/csrc/backward_mfma.hip", "transformer_attention_02_amd/csrc/mfma_tile.h",
                     "transformer_attention_02_amd/csrc/attn_internal.h"]
 DECODE_SOURCES = ["transformer_attention_02_amd/csrc/decode.hip", "transformer_attention_02_amd/csrc/attn_internal.h"]
@@ -190,6 +196,36 @@ class DecodeFp8(Decode):
                                     self.ws_bytes, stream)
         if st != bd.ATTN_OK:
             raise RuntimeError(f"attn_decode_fp8_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+
+class LatentDecode:
+    """attn_decode_latent_fwd on the latent-cache workload (inputs resident on the GPU)."""
+
+    def __init__(self, w, dev, bd, W, torch):
+        self.w, self.bd = w, bd
+        inp = W.latent_decode_inputs(w, device=dev)
+        self.inp = inp
+        self.q, self.cn = inp.q.to(dev), inp.c_new.to(dev)
+        self.wk, self.wv = inp.w_uk.to(dev), inp.w_uv.to(dev)
+        self.cc = inp.c_cache
+        self.lens = torch.from_numpy(inp.lens).to(dev)
+        self.Lmax = self.cc.shape[1]
+        self.out = torch.empty(w.B, w.H, w.hd, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(w.B, w.H, dtype=torch.float32, device=dev)
+        self.ws_bytes = bd.attn_decode_latent_workspace_bytes(w.B, w.H, w.dc, self.Lmax)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream, events=None):
+        w, bd = self.w, self.bd
+        if events:
+            bd.attn_set_timing_events(*events)
+        st = bd.attn_decode_latent_fwd(self.q.data_ptr(), self.cn.data_ptr(), self.cc.data_ptr(), self.lens.data_ptr(),
+                                       self.wk.data_ptr(), self.wv.data_ptr(), self.out.data_ptr(),
+                                       self.lse.data_ptr(), w.B, w.H, w.hd, w.dc, self.Lmax, w.alibi,
+                                       bd.ATTN_DTYPE_BF16, bd.ATTN_DTYPE_BF16, self.ws.data_ptr(), self.ws_bytes,
+                                       stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_decode_latent_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
 
 
 class Backward:
@@ -300,6 +336,33 @@ def cpu_baseline_fp8(dec8, seqs):
             "max_abs_err_vs_gpu_bf16_out": max(errs)}
 
 
+def cpu_baseline_latent(lat, seqs):
+    """The fp64 oracle of the latent decode step (explicit per-head keys and values) on the first sequences."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_decode_latent
+
+    w, inp = lat.w, lat.inp
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    pick = list(range(min(seqs, w.B)))
+    wk, wv = f64(lat.wk), f64(lat.wv)
+    t_total, nbytes, errs = 0.0, 0, []
+    for b in pick:
+        L = int(inp.lens[b])
+        cc = f64(lat.cc[b:b + 1, :L])
+        t0 = time.perf_counter()
+        ref = attention_decode_latent(f64(lat.q[b:b + 1]), f64(lat.cn[b:b + 1]), cc, np.array([L], dtype=np.int32),
+                                      wk, wv, alibi=w.alibi)[0]
+        t_total += time.perf_counter() - t0
+        nbytes += (L + 1) * w.dc * 2
+        errs.append(float(np.abs(f64(lat.out[b:b + 1]) - ref).max()))
+    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": nbytes / t_total / 1e9,
+            "unit": "GB/s", "seconds": t_total, "sample": f"sequences 0..{len(pick) - 1} of {w.B}",
+            "max_abs_err_vs_gpu_bf16_out": max(errs)}
+
+
 def cpu_baseline_bwd(bwd, heads):
     """The fp64 oracle backward on a bounded sample: the first ``heads`` query
     heads (whole GQA groups) of batch 0, all rows."""
@@ -333,8 +396,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "decode-fp8", "alibi", "small", "window", "chunk", "backward",
-                             "copy"],
+                    choices=["all", "prefill", "decode", "decode-fp8", "latent-decode", "alibi", "small", "window",
+                             "chunk", "backward", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -342,6 +405,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--cpu-heads-bwd", type=int, default=16)
+    ap.add_argument("--cpu-seqs-latent", type=int, default=8)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -384,6 +448,7 @@ def main():
     pre = Prefill(pre_w, dev, bd, W, torch) if pre_w is not None else None
     dec = Decode(W.KV_DECODE, dev, bd, W, torch) if args.workload in ("all", "decode", "decode-fp8") else None
     dec8 = DecodeFp8(W.KV_DECODE_FP8, dev, bd, W, torch) if args.workload == "decode-fp8" else None
+    lat = LatentDecode(W.LATENT_DECODE, dev, bd, W, torch) if args.workload == "latent-decode" else None
     stream = torch.cuda.current_stream().cuda_stream
     bwd = Backward(W.LLAMA3_8B, dev, bd, W, torch, stream) if args.workload == "backward" else None
     log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None} "
@@ -398,10 +463,12 @@ def main():
             bwd(stream)
         if dec8:
             dec8(stream)
+        if lat:
+            lat(stream)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk", "ec", "ek")}
+    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk", "ec", "ek", "lc", "lk")}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
@@ -414,6 +481,10 @@ def main():
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][0]), ctypes.c_void_p(stream))
             dec(stream, ev["dk"][i])
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["dc"][i][1]), ctypes.c_void_p(stream))
+        if lat:
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["lc"][i][0]), ctypes.c_void_p(stream))
+            lat(stream, ev["lk"][i])
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["lc"][i][1]), ctypes.c_void_p(stream))
         if dec8:
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["ec"][i][0]), ctypes.c_void_p(stream))
             dec8(stream, ev["ek"][i])
@@ -492,6 +563,21 @@ def main():
         cfg["bf16_cache"] = {"call_ms": bf["call_ms"], "kernel_ms": bf["kernel_ms"], "GB/s": bf["value"],
                              "kv_bytes": bf["kv_bytes"], "tokens_per_s": W.KV_DECODE.B / (bf["call_ms"] * 1e-3)}
         line["speedup_vs_bf16_cache"] = bf["call_ms"] / ec
+    if lat:
+        w = lat.w
+        lc, lk = avg("lc"), avg("lk")
+        gbs = w.cache_read_bytes() / (lc * 1e-3) / 1e9
+        kg = w.cache_read_bytes() / (lk * 1e-3) / 1e9
+        line.update(value=gbs, unit="GB/s", metric="latent-cache decode: cache-read GB/s, 1 GPU")
+        line["roofline"] = {"bound": "hbm", "achieved": kg, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": kg / PEAK_HBM_GBS, "traffic": traffic_for("latent_split", LATENT_SOURCES, w.name),
+                            "kernel": f"latent_split_kernel<{w.dc}>"}
+        cfg["workload"] = w.name
+        cfg["latent_decode"] = {"B": w.B, "H": w.H, "hd": w.hd, "dc": w.dc, "len_range": [w.len_lo, w.len_hi],
+                                "len_seed": w.len_seed, "Lmax": lat.Lmax, "cache_bytes": w.cache_read_bytes(),
+                                "weight_bytes": 2 * w.H * w.dc * w.hd * 2, "call_ms": lc, "kernel_ms": lk,
+                                "tokens_per_s": w.B / (lc * 1e-3)}
+        cfg["latent_decode"]["kernel_ms_median"], cfg["latent_decode"]["kernel_ms_min"] = med_min("lk")
     if bwd:
         w = bwd.w
         bc, bk = avg("bc"), avg("bk")
@@ -516,6 +602,8 @@ def main():
         ok &= bool(torch.isfinite(dec.out).all().item())
     if dec8:
         ok &= bool(torch.isfinite(dec8.out).all().item())
+    if lat:
+        ok &= bool(torch.isfinite(lat.out).all().item())
     if bwd:
         for t in (bwd.dq, bwd.dk, bwd.dv):
             ok &= bool(torch.isfinite(t).all().item())
@@ -545,7 +633,10 @@ def main():
                                      "prefill_kernel_vs_gemm": line["roofline"]["achieved"] / gemm}
         del a_, b_, c_
 
-    if not args.no_cpu_baseline and dec8:
+    if not args.no_cpu_baseline and lat:
+        log("cpu baseline: timing the fp64 oracle latent decode on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_latent(lat, args.cpu_seqs_latent)
+    elif not args.no_cpu_baseline and dec8:
         log("cpu baseline: timing the fp64 oracle fp8 decode on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline_fp8(dec8, args.cpu_seqs)
     elif not args.no_cpu_baseline and bwd:

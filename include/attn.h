@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -253,6 +253,43 @@ int attn_decode_fp8_fwd(const void* q, const void* k_new, const void* v_new, voi
                         int B, int H, int KV, int hd, int Lmax, double rope_base, int alibi,
                         float k_scale, float v_scale, int dtype, int out_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_latent_fwd needs (folded queries,
+ * split partials, merged latent outputs); 0 for non-positive sizes.
+ */
+size_t attn_decode_latent_workspace_bytes(int B, int H, int dc, int Lmax);
+
+/*
+ * One decode step with a latent cache ("Write attention from scratch",
+ * Exercise 5: keys and values are per-head up-projections of one short latent
+ * per token, and the key up-projection folds into the query). With the
+ * latent c_j of token j, head h's key is c_j W_uk[h] and its value c_j W_uv[h]:
+ *   s_hj = <q_h, c_j W_uk[h]> / sqrt(hd) (+ ALiBi bias -slope_h (L - j))
+ *        = <W_uk[h] q_h, c_j> / sqrt(hd),   out_h = (sum_j p_hj c_j) W_uv[h].
+ * No rotary embedding on this path (a rotation of the keys would not commute
+ * with the fold).
+ *
+ *   q          [B, H, hd]       bf16, the new token's queries
+ *   c_new      [B, dc]          bf16, its latent
+ *   c_cache    [B, Lmax, dc]    bf16, latents at slots 0..L-1 (read); slot L
+ *                               receives c_new (written)
+ *   cache_lens [B] int32 device L = cache_lens[b]; a sequence with L outside
+ *                               [0, Lmax) gets NaN and its cache is untouched
+ *   w_uk, w_uv [H, dc, hd]      bf16 up-projections (row c of W[h] maps latent
+ *                               dim c to the head's hd dims)
+ *   out        [B, H, hd]       out_dtype (written)
+ *   lse        [B, H]           fp32 (written; may be NULL), log-sum-exp of the
+ *                               scores over slots 0..L
+ *   workspace  at least attn_decode_latent_workspace_bytes(B, H, dc, Lmax)
+ * Supported: dtype ATTN_DTYPE_BF16, hd in {64, 128}, dc in {256, 512}, any H.
+ * Runs, in stream order: the query fold, the split-KV attention over the
+ * latent cache (which appends c_new), the merge and the value up-projection.
+ */
+int attn_decode_latent_fwd(const void* q, const void* c_new, void* c_cache, const int32_t* cache_lens,
+                           const void* w_uk, const void* w_uv, void* out, float* lse,
+                           int B, int H, int hd, int dc, int Lmax, int alibi, int dtype, int out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bd.attn_abi_version() == 3
+    assert bd.attn_abi_version() == 4
     names = {c: bd.attn_status_str(c) for c in range(7)}
     assert names == {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
                      4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP"}
@@ -213,6 +213,38 @@ def test_decode_fp8_validation(kw, code):
     assert st == code, (st, bd.attn_last_error())
 
 
+def _latent(**kw):
+    args = dict(q=FAKE, c_new=FAKE2, c_cache=FAKE3, cache_lens=FAKE4, w_uk=0x50000, w_uv=0x60000, out=0x70000,
+                lse=None, B=4, H=16, hd=128, dc=512, Lmax=4096, alibi=0, dtype=bd.ATTN_DTYPE_BF16,
+                out_dtype=bd.ATTN_DTYPE_F32, workspace=0x100000, workspace_bytes=1 << 26, stream=None)
+    args.update(kw)
+    return bd.attn_decode_latent_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w_uv=None), bd.ATTN_ERR_NULL),
+    (dict(c_cache=None), bd.ATTN_ERR_NULL),
+    (dict(H=0), bd.ATTN_ERR_SHAPE),
+    (dict(Lmax=512 * 512 + 1), bd.ATTN_ERR_SHAPE),
+    (dict(dtype=bd.ATTN_DTYPE_F32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(hd=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(dc=384), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(alibi=5), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(w_uk=0x50008), bd.ATTN_ERR_ALIGN),
+    (dict(workspace_bytes=1024), bd.ATTN_ERR_WORKSPACE),
+])
+def test_decode_latent_validation(kw, code):
+    st = _latent(**kw)
+    assert st == code, (st, bd.attn_last_error())
+
+
+def test_decode_latent_workspace_size():
+    n = bd.attn_decode_latent_workspace_bytes(64, 16, 512, 8193)
+    nsplit = -(-8193 // 512)
+    assert n >= 64 * 16 * (512 * 2 + nsplit * (512 * 4 + 8) + 512 * 4) and n % 256 == 0
+    assert bd.attn_decode_latent_workspace_bytes(0, 16, 512, 8193) == 0
+
+
 def test_decode_workspace_size():
     n = bd.attn_decode_workspace_bytes(64, 32, 8, 128, 8193)
     nsplit = -(-8193 // 256)
@@ -233,3 +265,4 @@ def test_launch_without_a_device_reports_hip_error():
     assert st == bd.ATTN_ERR_HIP
     assert "launch" in bd.attn_last_error()
     assert _decode_fp8() == bd.ATTN_ERR_HIP
+    assert _latent() == bd.ATTN_ERR_HIP

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_decode, attention_decode_fp8, attention_prefill, attention_prefill_bwd, e4m3_decode
+from oracle import (attention_decode, attention_decode_fp8, attention_decode_latent, attention_prefill,
+                    attention_prefill_bwd, e4m3_decode)
 from transformer_attention_02_amd import binding as bd
 from transformer_attention_02_amd import workloads as W
 
@@ -499,6 +500,66 @@ def test_decode_fp8_matches_bf16_decode_of_the_dequantized_cache():
     vd = (inp.v_cache.view(torch.float8_e4m3fn).float() * w.v_scale).to(torch.bfloat16)
     out16, lse16, _, _ = gpu_decode(W.DecodeInputs(inp.q, kn, vn, kd, vd, lens), 0.0)
     assert torch.allclose(out8, out16, rtol=0, atol=2e-3) and torch.allclose(lse8, lse16, rtol=0, atol=2e-3)
+
+
+# ---------------------------------------------------------- latent decode
+def gpu_decode_latent(inp: W.LatentInputs, alibi=0, out_dtype=torch.float32):
+    lens = torch.from_numpy(inp.lens).cuda()
+    cc = inp.c_cache.cuda()
+    B, H, hd = inp.q.shape
+    out = torch.full((B, H, hd), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+    bd.decode_latent(inp.q.cuda(), inp.c_new.cuda(), cc, lens, inp.w_uk.cuda(), inp.w_uv.cuda(), alibi=alibi,
+                     out=out, lse=lse, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, lse, cc.cpu()
+
+
+@pytest.mark.parametrize("H,hd,dc", [(16, 128, 512), (12, 64, 256), (40, 128, 256), (4, 64, 512)])
+@pytest.mark.parametrize("alibi", [0, 1])
+def test_decode_latent_ragged_lengths(H, hd, dc, alibi):
+    w = W.LatentDecodeWorkload("latent-small", 8, H, hd, dc, 0, 0, 5, 71 + H + dc)
+    lens = np.array([0, 1, 63, 64, 511, 512, 513, 1100], dtype=np.int32)
+    inp = W.latent_decode_inputs(w, lens=lens, lmax=1101)
+    print(f"[latent decode] H={H} hd={hd} dc={dc} alibi={alibi} lens={lens.tolist()}", flush=True)
+    out, lse, cc = gpu_decode_latent(inp, alibi)
+    ref, ref_lse, c_slot = attention_decode_latent(to64(inp.q), to64(inp.c_new), to64(inp.c_cache), lens,
+                                                   to64(inp.w_uk), to64(inp.w_uv), alibi=alibi)
+    err = np.abs(to64(out) - ref).max()
+    print(f"  max abs err {err:.3g} (output scale {np.abs(ref).max():.3g})", flush=True)
+    assert err <= 1e-2
+    assert np.abs(to64(lse) - ref_lse).max() <= 2e-2
+    cc64, c0 = to64(cc), to64(inp.c_cache)
+    for b, L in enumerate(lens):
+        assert np.array_equal(cc64[b, L], c_slot[b])
+        assert np.array_equal(cc64[b, :L], c0[b, :L]) and np.array_equal(cc64[b, L + 1:], c0[b, L + 1:])
+
+
+def test_decode_latent_full_size_sampled():
+    w = W.LATENT_DECODE
+    print(f"[full-size latent decode] {w.name}", flush=True)
+    inp = W.latent_decode_inputs(w)
+    out, lse, cc = gpu_decode_latent(inp, out_dtype=torch.bfloat16)
+    assert torch.isfinite(out).all().item()
+    lens = inp.lens
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 41})
+    ref, ref_lse, _ = attention_decode_latent(to64(inp.q), to64(inp.c_new), to64(inp.c_cache), lens, to64(inp.w_uk),
+                                              to64(inp.w_uv), batch=pick)
+    err = np.abs(to64(out[pick]) - ref).max()
+    print(f"  max abs err {err:.3g} (bf16 output)", flush=True)
+    assert err <= 1e-2
+    assert np.abs(to64(lse[pick]) - ref_lse).max() <= 2e-2
+
+
+def test_decode_latent_bad_length_gives_nan():
+    w = W.LatentDecodeWorkload("latent-bad", 3, 16, 128, 512, 0, 0, 5, 81)
+    lens = np.array([5, 300, 20], dtype=np.int32)
+    inp = W.latent_decode_inputs(w, lens=lens, lmax=301)
+    inp.lens[1] = 301   # == Lmax: out of range, must not fault or write
+    out, lse, cc = gpu_decode_latent(inp)
+    assert torch.isnan(out[1]).all() and torch.isnan(lse[1]).all()
+    assert torch.isfinite(out[[0, 2]]).all()
+    assert torch.equal(cc[1], inp.c_cache[1])
 
 
 def test_incremental_decode_equals_prefill():

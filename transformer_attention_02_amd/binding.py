@@ -45,6 +45,8 @@ EXPORTS = (
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
     "attn_decode_fp8_fwd",
+    "attn_decode_latent_workspace_bytes",
+    "attn_decode_latent_fwd",
 )
 
 _P = ctypes.c_void_p
@@ -69,6 +71,8 @@ _SIGS = {
     "attn_decode_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I, _P, _S, _P]),
     "attn_decode_fp8_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _F, _F, _I, _I, _P, _S,
                                  _P]),
+    "attn_decode_latent_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "attn_decode_latent_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
 }
 
 _lib = None
@@ -159,6 +163,16 @@ def attn_decode_fp8_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse,
     return load().attn_decode_fp8_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax,
                                       float(rope_base), alibi, float(k_scale), float(v_scale), dtype, out_dtype,
                                       workspace, workspace_bytes, stream)
+
+
+def attn_decode_latent_workspace_bytes(B, H, dc, Lmax) -> int:
+    return load().attn_decode_latent_workspace_bytes(B, H, dc, Lmax)
+
+
+def attn_decode_latent_fwd(q, c_new, c_cache, cache_lens, w_uk, w_uv, out, lse, B, H, hd, dc, Lmax, alibi, dtype,
+                           out_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().attn_decode_latent_fwd(q, c_new, c_cache, cache_lens, w_uk, w_uv, out, lse, B, H, hd, dc, Lmax,
+                                         alibi, dtype, out_dtype, workspace, workspace_bytes, stream)
 
 
 # --------------------------------------------------------------- torch helpers
@@ -312,5 +326,30 @@ def decode_fp8(q, k_new, v_new, k_cache, v_cache, cache_lens, k_scale, v_scale, 
                              lse.data_ptr() if lse is not None else None, B, H, KV, hd, Lmax, rope_base, alibi,
                              k_scale, v_scale, _dtype_code(q), _dtype_code(out), workspace.data_ptr(), nbytes,
                              _stream_ptr(stream))
+    _check(st)
+    return out, lse
+
+
+def decode_latent(q, c_new, c_cache, cache_lens, w_uk, w_uv, *, alibi=ATTN_ALIBI_NONE, out_dtype=None,
+                  want_lse=True, out=None, lse=None, workspace=None, stream=None):
+    """Run attn_decode_latent_fwd on GPU torch tensors (bf16). Returns (out, lse)."""
+    import torch
+
+    B, H, hd = q.shape
+    Lmax, dc = c_cache.shape[1], c_cache.shape[2]
+    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(B, H, hd, dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = attn_decode_latent_workspace_bytes(B, H, dc, Lmax)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = attn_decode_latent_fwd(q.data_ptr(), c_new.data_ptr(), c_cache.data_ptr(), cache_lens.data_ptr(),
+                                w_uk.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, H, hd, dc, Lmax, alibi,
+                                _dtype_code(q), _dtype_code(out), workspace.data_ptr(), nbytes, _stream_ptr(stream))
     _check(st)
     return out, lse

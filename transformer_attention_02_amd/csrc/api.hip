@@ -422,6 +422,89 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
 }
 }  // namespace
 
+namespace {
+// Workspace of the latent decode: [folded queries bf16][partials fp32][(m, l)][merged latent outputs fp32].
+struct LatentWs {
+  long long qt, part_o, part_ml, ot, total;
+};
+LatentWs latent_ws_layout(int B, int H, int dc, int Lmax) {
+  auto up = [](long long x) { return (x + 255) / 256 * 256; };
+  const long long nsplit = (Lmax + kLatentSplit - 1) / kLatentSplit;
+  const long long rows = (long long)B * H;
+  LatentWs w;
+  w.qt = 0;
+  w.part_o = up(rows * dc * 2);
+  w.part_ml = w.part_o + up(rows * nsplit * dc * 4);
+  w.ot = w.part_ml + up(rows * nsplit * 8);
+  w.total = w.ot + up(rows * dc * 4);
+  return w;
+}
+}  // namespace
+
+size_t attn_decode_latent_workspace_bytes(int B, int H, int dc, int Lmax) {
+  if (B <= 0 || H <= 0 || dc <= 0 || Lmax <= 0) return 0;
+  return (size_t)latent_ws_layout(B, H, dc, Lmax).total;
+}
+
+int attn_decode_latent_fwd(const void* q, const void* c_new, void* c_cache, const int32_t* cache_lens,
+                           const void* w_uk, const void* w_uv, void* out, float* lse, int B, int H, int hd, int dc,
+                           int Lmax, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!q || !c_new || !c_cache || !cache_lens || !w_uk || !w_uv || !out)
+    return fail(ATTN_ERR_NULL, "q, c_new, c_cache, cache_lens, w_uk, w_uv and out must be non-NULL");
+  if (B <= 0 || H <= 0 || Lmax <= 0 || hd <= 0 || dc <= 0)
+    return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d H=%d hd=%d dc=%d Lmax=%d)", B, H, hd, dc, Lmax);
+  if (B > 65535 || H > 65535) return fail(ATTN_ERR_SHAPE, "B and H must be <= 65535");
+  if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "latent decode takes bf16 inputs (dtype %d)", dtype);
+  if (out_dtype != ATTN_DTYPE_F32 && out_dtype != ATTN_DTYPE_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if (hd != 64 && hd != 128) return fail(ATTN_ERR_UNSUPPORTED, "hd %d (supported: 64, 128)", hd);
+  if (dc != 256 && dc != 512) return fail(ATTN_ERR_UNSUPPORTED, "latent width %d (supported: 256, 512)", dc);
+  if (alibi < ATTN_ALIBI_NONE || alibi > ATTN_ALIBI_PAGE1) return fail(ATTN_ERR_UNSUPPORTED, "alibi %d", alibi);
+  if ((Lmax + kLatentSplit - 1) / kLatentSplit > kLatentMaxSplits || (long long)Lmax * dc * 2 >= (1LL << 31))
+    return fail(ATTN_ERR_SHAPE, "Lmax=%d too large for the latent cache", Lmax);
+  if ((long long)B * Lmax * dc > kMaxElems) return fail(ATTN_ERR_SHAPE, "cache too large");
+  if (!aligned(q, 16) || !aligned(c_new, 16) || !aligned(c_cache, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
+      !aligned(out, 16))
+    return fail(ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(cache_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(ATTN_ERR_ALIGN, "cache_lens and lse must be 4-byte aligned");
+  const LatentWs lay = latent_ws_layout(B, H, dc, Lmax);
+  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace of %lld bytes required", lay.total);
+  if (workspace_bytes < (size_t)lay.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes < required %lld", workspace_bytes, lay.total);
+  if (!aligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  LatentArgs a;
+  memset(&a, 0, sizeof(a));
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.q = q;
+  a.c_new = c_new;
+  a.c_cache = c_cache;
+  a.lens = cache_lens;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.lse = lse;
+  a.qt = reinterpret_cast<uint16_t*>(ws + lay.qt);
+  a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+  a.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
+  a.ot = reinterpret_cast<float*>(ws + lay.ot);
+  a.B = B;
+  a.H = H;
+  a.hd = hd;
+  a.dc = dc;
+  a.Lmax = Lmax;
+  a.hblocks = (H + 15) / 16;
+  a.split = kLatentSplit;
+  a.nsplit = (Lmax + kLatentSplit - 1) / kLatentSplit;
+  a.alibi = alibi;
+  a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  const TimingHook tm = take_timing();
+  return hip_status(launch_decode_latent(a, reinterpret_cast<hipStream_t>(stream), tm), "latent decode launch");
+}
+
 int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
                     double rope_base, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,

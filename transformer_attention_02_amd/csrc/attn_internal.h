@@ -70,6 +70,29 @@ struct DecodeArgs {
   float k_scale, v_scale;
 };
 
+// Latent-attention decode (cache of one d_c-dim latent per token, shared by all heads).
+constexpr int kLatentSplit = 512;        // keys per split-KV partial (whole 16-key tiles)
+constexpr int kLatentMaxSplits = 512;    // splits per sequence the merge handles
+struct LatentArgs {
+  const void* q;         // [B,H,hd] bf16
+  const void* c_new;     // [B,dc] bf16
+  void* c_cache;         // [B,Lmax,dc] bf16
+  const int32_t* lens;   // [B]
+  const void* w_uk;      // [H,dc,hd] bf16
+  const void* w_uv;      // [H,dc,hd] bf16
+  void* out;             // [B,H,hd]
+  float* lse;            // [B,H] or nullptr
+  uint16_t* qt;          // [B,H,dc] bf16 folded queries (workspace)
+  float* part_o;         // [B,H,nsplit,dc] (workspace)
+  float2* part_ml;       // [B,H,nsplit]
+  float* ot;             // [B,H,dc] merged latent outputs (workspace)
+  int B, H, hd, dc, Lmax;
+  int hblocks;           // ceil(H / 16)
+  int split, nsplit;
+  int alibi, out_bf16;
+  float scale_log2;      // log2(e) / sqrt(hd)
+};
+
 struct BwdArgs {
   const void* q;     // [B,H,T,hd] rotated queries (workspace) or raw when rope is off
   const void* k;     // [B,KV,T,hd] rotated keys (workspace) or raw
@@ -123,6 +146,7 @@ hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkv_mfma(const BwdArgs& a, hipStream_t s);
 bool bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t s, const TimingHook& tm);
+hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t s, const TimingHook& tm);
 
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIPCC__)

@@ -106,6 +106,30 @@ class DecodeWorkload:
         return int(sum(int(L) + 1 for L in self.lengths()) * self.KV * self.hd * 2 * e)
 
 
+@dataclass(frozen=True)
+class LatentDecodeWorkload:
+    """Decode over a latent cache: one dc-dim latent per token shared by H heads,
+    per-head up-projections W_uk / W_uv [H, dc, hd] (bf16)."""
+    name: str
+    B: int
+    H: int
+    hd: int
+    dc: int
+    len_lo: int
+    len_hi: int
+    len_seed: int
+    seed: int
+    alibi: int = 0
+
+    def lengths(self) -> np.ndarray:
+        rng = np.random.default_rng(self.len_seed)
+        return rng.integers(self.len_lo, self.len_hi, size=self.B, endpoint=True).astype(np.int32)
+
+    def cache_read_bytes(self) -> int:
+        """Latent bytes the step must read: (len_b + 1) rows of dc bf16 per sequence."""
+        return int(sum(int(L) + 1 for L in self.lengths()) * self.dc * 2)
+
+
 TINY_FP32 = PrefillWorkload("tiny-fp32 T=6 H=4 KV=2 hd=8", 1, 6, 4, 2, 8, F32, 0, 10000.0)
 SMALL_BF16 = PrefillWorkload("small-bf16 B=1 T=512 H=8 KV=2 hd=64", 1, 512, 8, 2, 64, BF16, 2, 10000.0)
 LLAMA3_8B = PrefillWorkload("llama3-8b-prefill B=4 T=4096 H=32 KV=8 hd=128 rope=5e5",
@@ -125,6 +149,11 @@ KV_DECODE = DecodeWorkload("kv-decode B=64 len~U[512,8192] H=32 KV=8 hd=128",
 KV_DECODE_FP8 = DecodeWorkload("kv-decode fp8 E4M3 cache (scale 1/64) B=64 len~U[512,8192] H=32 KV=8 hd=128",
                                64, 32, 8, 128, 512, 8192, 5, 5, 10000.0, cache="fp8", k_scale=1 / 64,
                                v_scale=1 / 64)
+
+# latent-cache decode over the same 64 sequence lengths: 16 heads of 128 dims
+# up-projected from 512-number latents (the cache holds 1 KiB per token)
+LATENT_DECODE = LatentDecodeWorkload("latent-decode B=64 len~U[512,8192] H=16 hd=128 dc=512",
+                                     64, 16, 128, 512, 512, 8192, 5, 6)
 
 PREFILL_WORKLOADS = {"tiny": TINY_FP32, "small": SMALL_BF16, "llama3": LLAMA3_8B, "alibi": ALIBI_MHA,
                      "window": LLAMA3_WINDOW, "chunk": LLAMA3_CHUNK}
@@ -263,3 +292,34 @@ def to_e4m3_codes(x: torch.Tensor, scale: float) -> torch.Tensor:
     (round to nearest even), clamped to the finite range first; used only to
     synthesise fp8 cache contents."""
     return (x.float() / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+@dataclass
+class LatentInputs:
+    q: torch.Tensor        # [B, H, hd]
+    c_new: torch.Tensor    # [B, dc]
+    c_cache: torch.Tensor  # [B, Lmax, dc] (valid prefix per sequence; rest zero)
+    w_uk: torch.Tensor     # [H, dc, hd]
+    w_uv: torch.Tensor     # [H, dc, hd]
+    lens: np.ndarray       # [B]
+
+
+def latent_decode_inputs(w: LatentDecodeWorkload, *, lens: np.ndarray | None = None, lmax: int | None = None,
+                         device: str | torch.device = "cpu") -> LatentInputs:
+    """Seeded bf16 inputs: q, c_new, W_uk, W_uv (N(0,1), the weights scaled by
+    1/sqrt(dc) before rounding), then each sequence's latent prefix."""
+    if lens is None:
+        lens = w.lengths()
+    lens = np.asarray(lens, dtype=np.int32)
+    B = len(lens)
+    Lmax = int(lens.max()) + 1 if lmax is None else lmax
+    g = torch.Generator().manual_seed(w.seed)
+    q = normal_bf16(g, (B, w.H, w.hd))
+    c_new = normal_bf16(g, (B, w.dc))
+    w_uk = (torch.randn(w.H, w.dc, w.hd, generator=g) / np.sqrt(w.dc)).to(torch.bfloat16)
+    w_uv = (torch.randn(w.H, w.dc, w.hd, generator=g) / np.sqrt(w.dc)).to(torch.bfloat16)
+    c_cache = torch.zeros(B, Lmax, w.dc, dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        L = int(lens[b])
+        c_cache[b, :L] = normal_bf16(g, (L, w.dc)).to(device)
+    return LatentInputs(q, c_new, c_cache, w_uk, w_uv, lens)
