@@ -14,3 +14,4 @@ from .attention import (  # noqa: F401
 )
 from .fp8 import E4M3_MAX, attention_decode_fp8, e4m3_decode, e4m3_encode, e4m3_values  # noqa: F401
 from .latent import attention_decode_latent, fold_query  # noqa: F401
+from .proj import out_projection, proj_flops, qkv_projection, qkv_projection_to_cache  # noqa: F401
