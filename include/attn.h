@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -218,6 +218,11 @@ size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax);
  *   the query attends slots 0..L inclusive (ALiBi distance L - j).
  *   workspace: at least attn_decode_workspace_bytes(B, H, KV, hd, Lmax) bytes.
  *
+ * k_new and v_new may both be NULL: slot L of every sequence then already
+ * holds the new token's key (rotated) and value, as attn_qkv_proj_cache_fwd
+ * leaves them, and nothing is written to the caches. rope_base still applies
+ * to q; pass 0 when q comes rotated from that projection.
+ *
  * Runs, in stream order: the cache append, the split-KV partial kernel, and
  * the log-sum-exp merge of the partials.
  */
@@ -290,6 +295,61 @@ int attn_decode_latent_fwd(const void* q, const void* c_new, void* c_cache, cons
                            const void* w_uk, const void* w_uv, void* out, float* lse,
                            int B, int H, int hd, int dc, int Lmax, int alibi, int dtype, int out_dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused QKV input projection with rotary embedding ("Building Grouped-Query
+ * Attention with RoPE and Flash Attention from Scratch", Architecture Overview
+ * and Step 4: one projection of x emits q, k and v with fewer K/V heads than
+ * query heads, then q and k are rotated).
+ *
+ *   x      [B, T, D]            bf16, token t of sequence b
+ *   w_qkv  [(H + 2 KV) hd, D]   bf16: the rows of W_q (H hd), then W_k (KV hd),
+ *                               then W_v (KV hd), each an nn.Linear weight
+ *                               [out, in], so the projection is x w_qkv^T
+ *   q      [B, H,  T, hd]       bf16 (written), rotated at position pos0 + t
+ *   k      [B, KV, T, hd]       bf16 (written), rotated at position pos0 + t
+ *   v      [B, KV, T, hd]       bf16 (written)
+ *   rope_base: rotary base; 0 disables the rotation (interleaved pairs, the
+ *   same convention as attn_prefill_fwd, so q and k from here feed it with
+ *   rope_base 0).
+ * The products accumulate in fp32 on the matrix cores; the rotation is applied
+ * to the fp32 sums, which are then rounded once to bf16.
+ * Supported: dtype ATTN_DTYPE_BF16, hd in {64, 128}, D a multiple of 64 and
+ * every operand under 2 GiB (ATTN_ERR_UNSUPPORTED / ATTN_ERR_SHAPE otherwise).
+ * Pointers 16-byte aligned; x, w_qkv and the outputs must not overlap.
+ */
+int attn_qkv_proj_fwd(const void* x, const void* w_qkv, void* q, void* k, void* v,
+                      int B, int T, int D, int H, int KV, int hd, int pos0, double rope_base,
+                      int dtype, void* stream);
+
+/*
+ * The same projection for tokens appended to a KV cache (a decode step with
+ * T = 1, or a prompt chunk; the pre-allocated cache written by position of the
+ * GQA page's roadmap and lab Exercise 2 of "Write attention from scratch"):
+ * token t of sequence b sits at position L + t, L = cache_lens[b], and its
+ * rotated key and its value are written to slot L + t of k_cache / v_cache
+ * [B, KV, Lmax, hd] (bf16). q [B, H, T, hd] as above. A sequence with L < 0 or
+ * L + T > Lmax (checked on the device) gets NaN queries and its cache rows
+ * are not written. cache_lens is not modified. Other rules as
+ * attn_qkv_proj_fwd; requires 1 <= T <= Lmax.
+ */
+int attn_qkv_proj_cache_fwd(const void* x, const void* w_qkv, void* q, void* k_cache, void* v_cache,
+                            const int32_t* cache_lens, int B, int T, int D, int H, int KV, int hd, int Lmax,
+                            double rope_base, int dtype, void* stream);
+
+/*
+ * Output projection (the GQA page's Step 4: the attention output is
+ * transposed back to [B, T, H hd] and mixed by o_proj):
+ *   o    [B, H, T, hd]   bf16, the attention output
+ *   w_o  [D, H hd]       bf16, nn.Linear weight
+ *   y    [B, T, D]       out_dtype (written): y[b, t] = concat_h o[b, h, t] w_o^T
+ * The transpose is folded into the operand loads (o is read in place). fp32
+ * accumulation on the matrix cores, one rounding to out_dtype.
+ * Supported: dtype ATTN_DTYPE_BF16, out_dtype bf16 or fp32, hd in {64, 128},
+ * D a multiple of 64, operands under 2 GiB. Pointers 16-byte aligned.
+ */
+int attn_out_proj_fwd(const void* o, const void* w_o, void* y, int B, int T, int H, int hd, int D,
+                      int dtype, int out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

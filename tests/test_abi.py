@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bd.attn_abi_version() == 4
+    assert bd.attn_abi_version() == 5
     names = {c: bd.attn_status_str(c) for c in range(7)}
     assert names == {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
                      4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP"}
@@ -174,6 +174,10 @@ def _decode(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(cache_lens=None), bd.ATTN_ERR_NULL),
     (dict(k_cache=None), bd.ATTN_ERR_NULL),
+    (dict(k_new=None), bd.ATTN_ERR_NULL),          # one of k_new / v_new without the other
+    (dict(v_new=None), bd.ATTN_ERR_NULL),
+    (dict(k_new=None, v_new=None, Lmax=0), bd.ATTN_ERR_SHAPE),   # both NULL is the no-append form
+    (dict(k_new=None, v_new=None, k_cache=FAKE4 + 4), bd.ATTN_ERR_ALIGN),
     (dict(Lmax=0), bd.ATTN_ERR_SHAPE),
     (dict(H=8, KV=3), bd.ATTN_ERR_SHAPE),
     (dict(hd=48), bd.ATTN_ERR_UNSUPPORTED),
@@ -238,6 +242,79 @@ def test_decode_latent_validation(kw, code):
     assert st == code, (st, bd.attn_last_error())
 
 
+def test_decode_fp8_needs_the_new_token():
+    assert _decode_fp8(k_new=None, v_new=None) == bd.ATTN_ERR_NULL
+
+
+def _qkv(**kw):
+    args = dict(x=FAKE, w_qkv=FAKE2, q=FAKE3, k=FAKE4, v=0x50000, B=4, T=4096, D=4096, H=32, KV=8, hd=128, pos0=0,
+                rope_base=500000.0, dtype=bd.ATTN_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return bd.attn_qkv_proj_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), bd.ATTN_ERR_NULL),
+    (dict(v=None), bd.ATTN_ERR_NULL),
+    (dict(T=0), bd.ATTN_ERR_SHAPE),
+    (dict(H=32, KV=5), bd.ATTN_ERR_SHAPE),
+    (dict(pos0=-1), bd.ATTN_ERR_SHAPE),
+    (dict(B=64, T=8192), bd.ATTN_ERR_SHAPE),            # x would be 4 GiB
+    (dict(dtype=bd.ATTN_DTYPE_F32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(hd=32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(D=4000), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(rope_base=0.5), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(w_qkv=FAKE2 + 8), bd.ATTN_ERR_ALIGN),
+    (dict(k=FAKE4 + 2), bd.ATTN_ERR_ALIGN),
+])
+def test_qkv_proj_validation(kw, code):
+    st = _qkv(**kw)
+    assert st == code, (st, bd.attn_last_error())
+
+
+def _qkv_cache(**kw):
+    args = dict(x=FAKE, w_qkv=FAKE2, q=FAKE3, k_cache=FAKE4, v_cache=0x50000, cache_lens=0x60000, B=64, T=1, D=4096,
+                H=32, KV=8, hd=128, Lmax=8193, rope_base=500000.0, dtype=bd.ATTN_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return bd.attn_qkv_proj_cache_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cache_lens=None), bd.ATTN_ERR_NULL),
+    (dict(v_cache=None), bd.ATTN_ERR_NULL),
+    (dict(Lmax=0), bd.ATTN_ERR_SHAPE),
+    (dict(T=9000), bd.ATTN_ERR_SHAPE),                  # more tokens than cache slots
+    (dict(hd=64, D=100), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(cache_lens=0x60002), bd.ATTN_ERR_ALIGN),
+    (dict(k_cache=FAKE4 + 8), bd.ATTN_ERR_ALIGN),
+])
+def test_qkv_proj_cache_validation(kw, code):
+    st = _qkv_cache(**kw)
+    assert st == code, (st, bd.attn_last_error())
+
+
+def _outp(**kw):
+    args = dict(o=FAKE, w_o=FAKE2, y=FAKE3, B=4, T=4096, H=32, hd=128, D=4096, dtype=bd.ATTN_DTYPE_BF16,
+                out_dtype=bd.ATTN_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return bd.attn_out_proj_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(y=None), bd.ATTN_ERR_NULL),
+    (dict(B=0), bd.ATTN_ERR_SHAPE),
+    (dict(T=40000), bd.ATTN_ERR_SHAPE),                 # y in fp32 past 2 GiB at B=4
+    (dict(out_dtype=7), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=bd.ATTN_DTYPE_F32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(hd=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(D=4100), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(y=FAKE3 + 4), bd.ATTN_ERR_ALIGN),
+])
+def test_out_proj_validation(kw, code):
+    st = _outp(**kw)
+    assert st == code, (st, bd.attn_last_error())
+
+
 def test_decode_latent_workspace_size():
     n = bd.attn_decode_latent_workspace_bytes(64, 16, 512, 8193)
     nsplit = -(-8193 // 512)
@@ -266,3 +343,6 @@ def test_launch_without_a_device_reports_hip_error():
     assert "launch" in bd.attn_last_error()
     assert _decode_fp8() == bd.ATTN_ERR_HIP
     assert _latent() == bd.ATTN_ERR_HIP
+    assert _qkv() == bd.ATTN_ERR_HIP
+    assert _qkv_cache() == bd.ATTN_ERR_HIP
+    assert _outp(out_dtype=bd.ATTN_DTYPE_F32) == bd.ATTN_ERR_HIP

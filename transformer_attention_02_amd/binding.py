@@ -47,6 +47,9 @@ EXPORTS = (
     "attn_decode_fp8_fwd",
     "attn_decode_latent_workspace_bytes",
     "attn_decode_latent_fwd",
+    "attn_qkv_proj_fwd",
+    "attn_qkv_proj_cache_fwd",
+    "attn_out_proj_fwd",
 )
 
 _P = ctypes.c_void_p
@@ -73,6 +76,9 @@ _SIGS = {
                                  _P]),
     "attn_decode_latent_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_decode_latent_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "attn_qkv_proj_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _I, _P]),
+    "attn_qkv_proj_cache_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _I, _P]),
+    "attn_out_proj_fwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
 }
 
 _lib = None
@@ -173,6 +179,20 @@ def attn_decode_latent_fwd(q, c_new, c_cache, cache_lens, w_uk, w_uv, out, lse, 
                            out_dtype, workspace, workspace_bytes, stream) -> int:
     return load().attn_decode_latent_fwd(q, c_new, c_cache, cache_lens, w_uk, w_uv, out, lse, B, H, hd, dc, Lmax,
                                          alibi, dtype, out_dtype, workspace, workspace_bytes, stream)
+
+
+def attn_qkv_proj_fwd(x, w_qkv, q, k, v, B, T, D, H, KV, hd, pos0, rope_base, dtype, stream) -> int:
+    return load().attn_qkv_proj_fwd(x, w_qkv, q, k, v, B, T, D, H, KV, hd, pos0, float(rope_base), dtype, stream)
+
+
+def attn_qkv_proj_cache_fwd(x, w_qkv, q, k_cache, v_cache, cache_lens, B, T, D, H, KV, hd, Lmax, rope_base, dtype,
+                            stream) -> int:
+    return load().attn_qkv_proj_cache_fwd(x, w_qkv, q, k_cache, v_cache, cache_lens, B, T, D, H, KV, hd, Lmax,
+                                          float(rope_base), dtype, stream)
+
+
+def attn_out_proj_fwd(o, w_o, y, B, T, H, hd, D, dtype, out_dtype, stream) -> int:
+    return load().attn_out_proj_fwd(o, w_o, y, B, T, H, hd, D, dtype, out_dtype, stream)
 
 
 # --------------------------------------------------------------- torch helpers
@@ -279,7 +299,9 @@ def decode_workspace(B, H, KV, hd, Lmax, device):
 
 def decode(q, k_new, v_new, k_cache, v_cache, cache_lens, *, rope_base=10000.0, alibi=ATTN_ALIBI_NONE,
            out_dtype=None, want_lse=True, out=None, lse=None, workspace=None, stream=None):
-    """Run attn_decode_fwd on GPU torch tensors (see include/attn.h for shapes). Returns (out, lse)."""
+    """Run attn_decode_fwd on GPU torch tensors (see include/attn.h for shapes). Returns (out, lse).
+
+    k_new = v_new = None: slot cache_lens[b] already holds the new token (see attn_qkv_proj_cache_fwd)."""
     import torch
 
     B, H, hd = q.shape
@@ -295,7 +317,8 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_lens, *, rope_base=10000.0, 
         workspace, nbytes = decode_workspace(B, H, KV, hd, Lmax, q.device)
     else:
         nbytes = workspace.numel() * workspace.element_size()
-    st = attn_decode_fwd(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+    st = attn_decode_fwd(q.data_ptr(), None if k_new is None else k_new.data_ptr(),
+                         None if v_new is None else v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                          cache_lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
                          B, H, KV, hd, Lmax, rope_base, alibi, dt, _dtype_code(out), workspace.data_ptr(), nbytes,
                          _stream_ptr(stream))
@@ -353,3 +376,46 @@ def decode_latent(q, c_new, c_cache, cache_lens, w_uk, w_uv, *, alibi=ATTN_ALIBI
                                 _dtype_code(q), _dtype_code(out), workspace.data_ptr(), nbytes, _stream_ptr(stream))
     _check(st)
     return out, lse
+
+
+def qkv_proj(x, w_qkv, H, KV, *, pos0=0, rope_base=10000.0, stream=None):
+    """attn_qkv_proj_fwd on GPU bf16 tensors x [B,T,D], w_qkv [(H+2KV)hd, D]. Returns (q, k, v)."""
+    import torch
+
+    B, T, D = x.shape
+    hd = w_qkv.shape[0] // (H + 2 * KV)
+    q = torch.empty(B, H, T, hd, dtype=torch.bfloat16, device=x.device)
+    k = torch.empty(B, KV, T, hd, dtype=torch.bfloat16, device=x.device)
+    v = torch.empty(B, KV, T, hd, dtype=torch.bfloat16, device=x.device)
+    st = attn_qkv_proj_fwd(x.data_ptr(), w_qkv.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, D, H, KV,
+                           hd, pos0, rope_base, _dtype_code(x), _stream_ptr(stream))
+    _check(st)
+    return q, k, v
+
+
+def qkv_proj_cache(x, w_qkv, k_cache, v_cache, cache_lens, H, *, rope_base=10000.0, stream=None):
+    """attn_qkv_proj_cache_fwd: k/v of the T new tokens go to slots cache_lens[b] + t. Returns q."""
+    import torch
+
+    B, T, D = x.shape
+    KV, Lmax, hd = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
+    q = torch.empty(B, H, T, hd, dtype=torch.bfloat16, device=x.device)
+    st = attn_qkv_proj_cache_fwd(x.data_ptr(), w_qkv.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 cache_lens.data_ptr(), B, T, D, H, KV, hd, Lmax, rope_base, _dtype_code(x),
+                                 _stream_ptr(stream))
+    _check(st)
+    return q
+
+
+def out_proj(o, w_o, *, out_dtype=None, stream=None):
+    """attn_out_proj_fwd on GPU tensors o [B,H,T,hd] bf16, w_o [D, H*hd] bf16. Returns y [B,T,D]."""
+    import torch
+
+    B, H, T, hd = o.shape
+    D = w_o.shape[0]
+    y = torch.empty(B, T, D, dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=o.device)
+    st = attn_out_proj_fwd(o.data_ptr(), w_o.data_ptr(), y.data_ptr(), B, T, H, hd, D, _dtype_code(o), _dtype_code(y),
+                           _stream_ptr(stream))
+    _check(st)
+    return y

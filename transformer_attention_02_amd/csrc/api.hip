@@ -360,15 +360,19 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
                 const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
                 double rope_base, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,
                 void* stream, int fp8, float k_scale, float v_scale) {
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !out)
-    return fail(ATTN_ERR_NULL, "q, k_new, v_new, k_cache, v_cache, cache_lens and out must be non-NULL");
+  if (!q || !k_cache || !v_cache || !cache_lens || !out)
+    return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, cache_lens and out must be non-NULL");
+  // k_new and v_new both NULL: slot L already holds the new token (bf16/fp32 caches only)
+  const bool append = k_new || v_new;
+  if (append && (!k_new || !v_new)) return fail(ATTN_ERR_NULL, "k_new and v_new must both be given or both be NULL");
+  if (!append && fp8) return fail(ATTN_ERR_NULL, "the fp8 cache needs k_new and v_new");
   if (B <= 0 || H <= 0 || KV <= 0 || Lmax <= 0)
     return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d H=%d KV=%d Lmax=%d)", B, H, KV, Lmax);
   if (H % KV) return fail(ATTN_ERR_SHAPE, "H=%d is not a multiple of KV=%d", H, KV);
   if (H > 65535 || B > 65535 || KV > 65535) return fail(ATTN_ERR_SHAPE, "H, KV and B must be <= 65535");
   if (int c = check_common(dtype, out_dtype, alibi, rope_base, hd)) return c;
   if ((long long)B * KV * Lmax * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "cache too large");
-  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+  if (!aligned(q, 16) || (append && (!aligned(k_new, 16) || !aligned(v_new, 16))) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(out, 16))
     return fail(ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(cache_lens, 4) || (lse && !aligned(lse, 4)))
@@ -408,6 +412,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
   a.fp8 = fp8;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.append = append;
   if (fp8) {
     if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
       return fail(ATTN_ERR_SHAPE, "k_scale and v_scale must be positive and finite (%g, %g)", (double)k_scale,
@@ -522,3 +527,116 @@ int attn_decode_fp8_fwd(const void* q, const void* k_new, const void* v_new, voi
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ projections
+#include "proj_internal.h"
+
+namespace {
+// Checks shared by the projections; M = B*T rows of K inputs, N outputs.
+int proj_checks(int B, int T, int H, int KV, int hd, int D, int dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || KV <= 0 || hd <= 0 || D <= 0)
+    return fail(ATTN_ERR_SHAPE, "sizes must be positive (B=%d T=%d D=%d H=%d KV=%d hd=%d)", B, T, D, H, KV, hd);
+  if (H % KV) return fail(ATTN_ERR_SHAPE, "H=%d is not a multiple of KV=%d", H, KV);
+  if (hd % 2) return fail(ATTN_ERR_SHAPE, "head dim %d must be even", hd);
+  if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "projections take bf16 (dtype %d)", dtype);
+  if (hd != 64 && hd != 128) return fail(ATTN_ERR_UNSUPPORTED, "projections support head dim 64 or 128 (got %d)", hd);
+  if (D % 64) return fail(ATTN_ERR_UNSUPPORTED, "model dim %d must be a multiple of 64", D);
+  const long long M = (long long)B * T, N = (long long)(H + 2 * KV) * hd;
+  if (M * D * 2 >= (1LL << 31) || N * D * 2 >= (1LL << 31) || M * H * hd * 2 >= (1LL << 31) ||
+      (long long)D * H * hd * 2 >= (1LL << 31))
+    return fail(ATTN_ERR_SHAPE, "every operand must be under 2 GiB");
+  return ATTN_OK;
+}
+
+int qkv_impl(const void* x, const void* w, void* q, void* k, void* v, void* k_cache, void* v_cache,
+             const int32_t* lens, int B, int T, int D, int H, int KV, int hd, int Lmax, int pos0, double rope_base,
+             int dtype, void* stream, int mode) {
+  if (int c = proj_checks(B, T, H, KV, hd, D, dtype)) return c;
+  if (!(rope_base == 0.0 || rope_base > 1.0) || !std::isfinite(rope_base))
+    return fail(ATTN_ERR_UNSUPPORTED, "rope_base %g (0 disables, otherwise > 1)", rope_base);
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16)) return fail(ATTN_ERR_ALIGN, "tensors must be 16-byte aligned");
+  ProjArgs a;
+  memset(&a, 0, sizeof(a));
+  if (mode == PROJ_QKV_CACHE) {
+    if (Lmax <= 0 || T > Lmax) return fail(ATTN_ERR_SHAPE, "Lmax=%d must be positive and >= T=%d", Lmax, T);
+    if ((long long)B * KV * Lmax * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "cache too large");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(lens, 4))
+      return fail(ATTN_ERR_ALIGN, "caches must be 16-byte aligned and cache_lens 4-byte aligned");
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.lens = lens;
+    a.Lmax = Lmax;
+  } else {
+    if (pos0 < 0 || (long long)pos0 + T > 0x7fffffffLL) return fail(ATTN_ERR_SHAPE, "pos0=%d out of range", pos0);
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(ATTN_ERR_ALIGN, "tensors must be 16-byte aligned");
+    a.k = k;
+    a.v = v;
+    a.pos0 = pos0;
+  }
+  a.a = x;
+  a.w = w;
+  a.M = B * T;
+  a.N = (H + 2 * KV) * hd;
+  a.K = D;
+  a.T = T;
+  a.H = H;
+  a.KV = KV;
+  a.hd = hd;
+  a.a_bytes = (unsigned)((long long)a.M * D * 2);
+  a.w_bytes = (unsigned)((long long)a.N * D * 2);
+  a.q = q;
+  a.rope = rope_base != 0.0;
+  a.freqs = make_freqs(hd, rope_base);
+  const TimingHook tm = take_timing();
+  return hip_status(launch_proj(a, mode, reinterpret_cast<hipStream_t>(stream), tm), "projection launch");
+}
+}  // namespace
+
+int attn_qkv_proj_fwd(const void* x, const void* w_qkv, void* q, void* k, void* v, int B, int T, int D, int H,
+                      int KV, int hd, int pos0, double rope_base, int dtype, void* stream) {
+  if (!x || !w_qkv || !q || !k || !v) return fail(ATTN_ERR_NULL, "x, w_qkv, q, k and v must be non-NULL");
+  if (int c = qkv_impl(x, w_qkv, q, k, v, nullptr, nullptr, nullptr, B, T, D, H, KV, hd, 0, pos0, rope_base, dtype,
+                       stream, PROJ_QKV))
+    return c;
+  return ok();
+}
+
+int attn_qkv_proj_cache_fwd(const void* x, const void* w_qkv, void* q, void* k_cache, void* v_cache,
+                            const int32_t* cache_lens, int B, int T, int D, int H, int KV, int hd, int Lmax,
+                            double rope_base, int dtype, void* stream) {
+  if (!x || !w_qkv || !q || !k_cache || !v_cache || !cache_lens)
+    return fail(ATTN_ERR_NULL, "x, w_qkv, q, k_cache, v_cache and cache_lens must be non-NULL");
+  if (int c = qkv_impl(x, w_qkv, q, nullptr, nullptr, k_cache, v_cache, cache_lens, B, T, D, H, KV, hd, Lmax, 0,
+                       rope_base, dtype, stream, PROJ_QKV_CACHE))
+    return c;
+  return ok();
+}
+
+int attn_out_proj_fwd(const void* o, const void* w_o, void* y, int B, int T, int H, int hd, int D, int dtype,
+                      int out_dtype, void* stream) {
+  if (!o || !w_o || !y) return fail(ATTN_ERR_NULL, "o, w_o and y must be non-NULL");
+  if (int c = proj_checks(B, T, H, H, hd, D, dtype)) return c;
+  if (out_dtype != ATTN_DTYPE_F32 && out_dtype != ATTN_DTYPE_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if ((long long)B * T * D * 4 >= (1LL << 31)) return fail(ATTN_ERR_SHAPE, "every operand must be under 2 GiB");
+  if (!aligned(o, 16) || !aligned(w_o, 16) || !aligned(y, 16)) return fail(ATTN_ERR_ALIGN, "tensors must be 16-byte aligned");
+  ProjArgs a;
+  memset(&a, 0, sizeof(a));
+  a.a = o;
+  a.w = w_o;
+  a.M = B * T;
+  a.N = D;
+  a.K = H * hd;
+  a.T = T;
+  a.H = H;
+  a.KV = H;
+  a.hd = hd;
+  a.a_bytes = (unsigned)((long long)B * H * T * hd * 2);
+  a.w_bytes = (unsigned)((long long)D * H * hd * 2);
+  a.y = y;
+  a.out_bf16 = out_dtype == ATTN_DTYPE_BF16;
+  const TimingHook tm = take_timing();
+  if (int c = hip_status(launch_proj(a, PROJ_OUT, reinterpret_cast<hipStream_t>(stream), tm), "projection launch"))
+    return c;
+  return ok();
+}

@@ -68,6 +68,7 @@ struct DecodeArgs {
   RopeFreqs freqs;
   int fp8;               // caches hold OCP E4M3 codes (value = code * scale)
   float k_scale, v_scale;
+  int append;            // 1: write k_new/v_new to slot L; 0: slot L already holds them
 };
 
 // Latent-attention decode (cache of one d_c-dim latent per token, shared by all heads).

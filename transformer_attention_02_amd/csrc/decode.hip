@@ -271,7 +271,7 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   // This split holds the new token's slot L: its workgroup writes the rotated
   // key and the value to the cache, and the wave whose tile covers slot L
   // patches that row of its LDS tile (it never reads slot L back from memory).
-  const bool own_slot = L >= k0 && L < k0 + SPLIT;
+  const bool own_slot = a.append && L >= k0 && L < k0 + SPLIT;
   uint32_t knew = 0, vnew = 0;  // lane p < HD/2: pair p of R(L) k_new and v_new (bf16x2, as read back)
   const long cslot = (((long)b * a.KV + kvh) * a.Lmax + L) * HD;
   const long nslot = ((long)b * a.KV + kvh) * HD;
@@ -549,7 +549,7 @@ hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHoo
   a.split = mfma ? (fp8_split ? kSplitMfmaFp8 : (long_split ? kSplitMfmaLong : kSplitMfma)) : kDecodeSplit;
   a.nsplit = (a.Lmax + a.split - 1) / a.split;
   hipError_t e = hipSuccess;
-  if (!mfma) {  // the MFMA split kernel appends the new token itself
+  if (!mfma && a.append) {  // the MFMA split kernel appends the new token itself
     hipLaunchKernelGGL(decode_append_kernel<BF16>, dim3(a.KV, a.B), dim3(HD / 2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

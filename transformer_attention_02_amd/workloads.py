@@ -130,6 +130,36 @@ class LatentDecodeWorkload:
         return int(sum(int(L) + 1 for L in self.lengths()) * self.dc * 2)
 
 
+@dataclass(frozen=True)
+class ProjWorkload:
+    """The projections either side of attention: x [B, T, D] -> q/k/v heads
+    (w_qkv [(H+2KV)hd, D]) and the attention output [B, H, T, hd] -> y [B, T, D]
+    (w_o [D, H hd]); bf16."""
+    name: str
+    B: int
+    T: int
+    D: int
+    H: int
+    KV: int
+    hd: int
+    rope_base: float
+    seed: int
+
+    @property
+    def M(self) -> int:
+        return self.B * self.T
+
+    @property
+    def N_qkv(self) -> int:
+        return (self.H + 2 * self.KV) * self.hd
+
+    def qkv_flops(self) -> float:
+        return 2.0 * self.M * self.N_qkv * self.D
+
+    def out_flops(self) -> float:
+        return 2.0 * self.M * self.D * self.H * self.hd
+
+
 TINY_FP32 = PrefillWorkload("tiny-fp32 T=6 H=4 KV=2 hd=8", 1, 6, 4, 2, 8, F32, 0, 10000.0)
 SMALL_BF16 = PrefillWorkload("small-bf16 B=1 T=512 H=8 KV=2 hd=64", 1, 512, 8, 2, 64, BF16, 2, 10000.0)
 LLAMA3_8B = PrefillWorkload("llama3-8b-prefill B=4 T=4096 H=32 KV=8 hd=128 rope=5e5",
@@ -154,6 +184,10 @@ KV_DECODE_FP8 = DecodeWorkload("kv-decode fp8 E4M3 cache (scale 1/64) B=64 len~U
 # up-projected from 512-number latents (the cache holds 1 KiB per token)
 LATENT_DECODE = LatentDecodeWorkload("latent-decode B=64 len~U[512,8192] H=16 hd=128 dc=512",
                                      64, 16, 128, 512, 512, 8192, 5, 6)
+
+# the projections of the Llama-3-8B prefill shape: D = 4096 = 32 x 128, 8 KV heads
+PROJ_LLAMA3_8B = ProjWorkload("llama3-8b projections B=4 T=4096 D=4096 H=32 KV=8 hd=128 rope=5e5",
+                              4, 4096, 4096, 32, 8, 128, 500000.0, 7)
 
 PREFILL_WORKLOADS = {"tiny": TINY_FP32, "small": SMALL_BF16, "llama3": LLAMA3_8B, "alibi": ALIBI_MHA,
                      "window": LLAMA3_WINDOW, "chunk": LLAMA3_CHUNK}
@@ -323,3 +357,24 @@ def latent_decode_inputs(w: LatentDecodeWorkload, *, lens: np.ndarray | None = N
         L = int(lens[b])
         c_cache[b, :L] = normal_bf16(g, (L, w.dc)).to(device)
     return LatentInputs(q, c_new, c_cache, w_uk, w_uv, lens)
+
+
+@dataclass
+class ProjInputs:
+    x: torch.Tensor      # [B, T, D]
+    w_qkv: torch.Tensor  # [(H + 2KV) hd, D]
+    o: torch.Tensor      # [B, H, T, hd], an attention output to project back
+    w_o: torch.Tensor    # [D, H hd]
+
+
+def proj_inputs(w: ProjWorkload, *, B: int | None = None, T: int | None = None) -> ProjInputs:
+    """Seeded bf16 inputs: x and o N(0,1); weights N(0,1) scaled by 1/sqrt(fan-in)
+    before rounding (the scale of nn.Linear's default initialisation)."""
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    g = torch.Generator().manual_seed(w.seed)
+    x = normal_bf16(g, (B, T, w.D))
+    w_qkv = (torch.randn(w.N_qkv, w.D, generator=g) / np.sqrt(w.D)).to(torch.bfloat16)
+    o = normal_bf16(g, (B, w.H, T, w.hd))
+    w_o = (torch.randn(w.D, w.H * w.hd, generator=g) / np.sqrt(w.H * w.hd)).to(torch.bfloat16)
+    return ProjInputs(x, w_qkv, o, w_o)
