@@ -29,8 +29,16 @@ instead (bf16 gradients; ``value`` = backward TFLOP/s with the algorithmic
 10*B*H*hd*T(T+1)/2 flops; ``roofline`` covers its two matrix-core kernels,
 dq and dk/dv, timed together).
 
+``--workload proj`` times the projections either side of attention on the
+Llama-3-8B prefill shape (B=4, T=4096, D=4096, H=32, KV=8, hd=128):
+attn_qkv_proj_fwd (fused QKV projection, RoPE of q and k, head split) then
+attn_out_proj_fwd (head merge, output projection); ``value`` = TFLOP/s of the
+pair, ``roofline`` covers the QKV kernel, and the same two GEMMs through
+torch.matmul (the vendor library, without the epilogue work) are timed in the
+same run as context.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload all|prefill|decode|decode-fp8|latent-decode|alibi|small|window|chunk|backward|copy]
+                       [--workload all|prefill|decode|decode-fp8|latent-decode|proj|alibi|small|window|chunk|backward|copy]
                        [--no-cpu-baseline] [--no-ceilings]
 """
 from __future__ import annotations
@@ -113,6 +121,8 @@ def traffic_for(kernel, sources, workload):
     return ent.get("bytes_per_launch")
 
 
+PROJ_SOURCES = ["transformer_attention_02_amd/csrc/proj.hip", "transformer_attention_02_amd/csrc/proj_internal.h",
+                "transformer_attention_02_amd/csrc/mfma_tile.h", "transformer_attention_02_amd/csrc/attn_internal.h"]
 PREFILL_SOURCES = ["transformer_attention_02_amd/csrc/prefill_mfma.hip", "transformer_attention_02_amd/csrc/mfma_tile.h",
                    "transformer_attention_02_amd/csrc/attn_internal.h"]
 LATENT_SOURCES = ["transformer_attention_02_amd/csrc/decode_latent.hip", "transformer_attention_02_amd/csrc/mfma_tile.h",
@@ -226,6 +236,56 @@ class LatentDecode:
                                        stream)
         if st != bd.ATTN_OK:
             raise RuntimeError(f"attn_decode_latent_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+
+class Proj:
+    """attn_qkv_proj_fwd then attn_out_proj_fwd (inputs resident on the GPU); each kernel timed."""
+
+    def __init__(self, w, dev, bd, W, torch):
+        self.w, self.bd = w, bd
+        inp = W.proj_inputs(w)
+        self.x, self.wq = inp.x.to(dev), inp.w_qkv.to(dev)
+        self.o, self.wo = inp.o.to(dev), inp.w_o.to(dev)
+        bf = torch.bfloat16
+        self.q = torch.empty(w.B, w.H, w.T, w.hd, dtype=bf, device=dev)
+        self.k = torch.empty(w.B, w.KV, w.T, w.hd, dtype=bf, device=dev)
+        self.v = torch.empty(w.B, w.KV, w.T, w.hd, dtype=bf, device=dev)
+        self.y = torch.empty(w.B, w.T, w.D, dtype=bf, device=dev)
+
+    def __call__(self, stream, ev_qkv=None, ev_out=None):
+        w, bd = self.w, self.bd
+        if ev_qkv:
+            bd.attn_set_timing_events(*ev_qkv)
+        st = bd.attn_qkv_proj_fwd(self.x.data_ptr(), self.wq.data_ptr(), self.q.data_ptr(), self.k.data_ptr(),
+                                  self.v.data_ptr(), w.B, w.T, w.D, w.H, w.KV, w.hd, 0, w.rope_base,
+                                  bd.ATTN_DTYPE_BF16, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_qkv_proj_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+        if ev_out:
+            bd.attn_set_timing_events(*ev_out)
+        st = bd.attn_out_proj_fwd(self.o.data_ptr(), self.wo.data_ptr(), self.y.data_ptr(), w.B, w.T, w.H, w.hd, w.D,
+                                  bd.ATTN_DTYPE_BF16, bd.ATTN_DTYPE_BF16, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_out_proj_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+    def library_gemms(self, torch, reps=10):
+        """The same two GEMMs through torch.matmul (no rotation, no head split): ms each."""
+        w = self.w
+        x2 = self.x.view(w.M, w.D)
+        o2 = self.o.transpose(1, 2).contiguous().view(w.M, w.H * w.hd)
+        out = {}
+        for name, f in (("qkv", lambda: torch.matmul(x2, self.wq.t())), ("out", lambda: torch.matmul(o2, self.wo.t()))):
+            for _ in range(3):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            out[name] = e0.elapsed_time(e1) / reps
+        return out
 
 
 class Backward:
@@ -363,6 +423,34 @@ def cpu_baseline_latent(lat, seqs):
             "max_abs_err_vs_gpu_bf16_out": max(errs)}
 
 
+def cpu_baseline_proj(pj, seqs):
+    """The fp64 oracle of both projections (numpy matmul, RoPE, head split / merge) on the first sequences,
+    checked against the GPU's outputs."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import out_projection, qkv_projection
+
+    w = pj.w
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    wq, wo = f64(pj.wq), f64(pj.wo)
+    n = min(seqs, w.B)
+    secs, err = 0.0, 0.0
+    for b in range(n):
+        x, o = f64(pj.x[b:b + 1]), f64(pj.o[b:b + 1])
+        t0 = time.perf_counter()
+        q, k, v = qkv_projection(x, wq, H=w.H, KV=w.KV, hd=w.hd, rope_base=w.rope_base)
+        y = out_projection(o, wo)
+        secs += time.perf_counter() - t0
+        err = max(err, float(np.abs(f64(pj.q[b:b + 1]) - q).max()), float(np.abs(f64(pj.k[b:b + 1]) - k).max()),
+                  float(np.abs(f64(pj.v[b:b + 1]) - v).max()), float(np.abs(f64(pj.y[b:b + 1]) - y).max()))
+    flops = n * w.T * (2.0 * w.N_qkv * w.D + 2.0 * w.D * w.H * w.hd)
+    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": flops / secs / 1e12,
+            "unit": "TFLOP/s", "seconds": secs, "sample": f"sequences 0..{n - 1} of {w.B} (both projections)",
+            "max_abs_err_vs_gpu_bf16": err}
+
+
 def cpu_baseline_bwd(bwd, heads):
     """The fp64 oracle backward on a bounded sample: the first ``heads`` query
     heads (whole GQA groups) of batch 0, all rows."""
@@ -396,8 +484,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "decode-fp8", "latent-decode", "alibi", "small", "window",
-                             "chunk", "backward", "copy"],
+                    choices=["all", "prefill", "decode", "decode-fp8", "latent-decode", "proj", "alibi", "small",
+                             "window", "chunk", "backward", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -406,6 +494,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--cpu-heads-bwd", type=int, default=16)
     ap.add_argument("--cpu-seqs-latent", type=int, default=8)
+    ap.add_argument("--cpu-seqs-proj", type=int, default=4)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -449,6 +538,7 @@ def main():
     dec = Decode(W.KV_DECODE, dev, bd, W, torch) if args.workload in ("all", "decode", "decode-fp8") else None
     dec8 = DecodeFp8(W.KV_DECODE_FP8, dev, bd, W, torch) if args.workload == "decode-fp8" else None
     lat = LatentDecode(W.LATENT_DECODE, dev, bd, W, torch) if args.workload == "latent-decode" else None
+    pj = Proj(W.PROJ_LLAMA3_8B, dev, bd, W, torch) if args.workload == "proj" else None
     stream = torch.cuda.current_stream().cuda_stream
     bwd = Backward(W.LLAMA3_8B, dev, bd, W, torch, stream) if args.workload == "backward" else None
     log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None} "
@@ -465,10 +555,13 @@ def main():
             dec8(stream)
         if lat:
             lat(stream)
+        if pj:
+            pj(stream)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk", "ec", "ek", "lc", "lk")}
+    ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk", "ec", "ek", "lc", "lk",
+                                                                     "jc", "jq", "jo")}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
@@ -485,6 +578,10 @@ def main():
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["lc"][i][0]), ctypes.c_void_p(stream))
             lat(stream, ev["lk"][i])
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["lc"][i][1]), ctypes.c_void_p(stream))
+        if pj:
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["jc"][i][0]), ctypes.c_void_p(stream))
+            pj(stream, ev["jq"][i], ev["jo"][i])
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["jc"][i][1]), ctypes.c_void_p(stream))
         if dec8:
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["ec"][i][0]), ctypes.c_void_p(stream))
             dec8(stream, ev["ek"][i])
@@ -578,6 +675,26 @@ def main():
                                 "weight_bytes": 2 * w.H * w.dc * w.hd * 2, "call_ms": lc, "kernel_ms": lk,
                                 "tokens_per_s": w.B / (lc * 1e-3)}
         cfg["latent_decode"]["kernel_ms_median"], cfg["latent_decode"]["kernel_ms_min"] = med_min("lk")
+    if pj:
+        w = pj.w
+        jc, jq, jo = avg("jc"), avg("jq"), avg("jo")
+        fl = w.qkv_flops() + w.out_flops()
+        kq = w.qkv_flops() / (jq * 1e-3) / 1e12
+        line.update(value=fl / (jc * 1e-3) / 1e12, unit="TFLOP/s",
+                    metric="QKV projection (RoPE, head split) + output projection TFLOP/s, 1 GPU")
+        cfg["workload"] = w.name
+        lib = pj.library_gemms(torch)
+        cfg["proj"] = {"B": w.B, "T": w.T, "D": w.D, "H": w.H, "KV": w.KV, "hd": w.hd, "rope_base": w.rope_base,
+                       "qkv_flops": w.qkv_flops(), "out_flops": w.out_flops(), "call_ms": jc,
+                       "qkv_kernel_ms": jq, "out_kernel_ms": jo,
+                       "qkv_kernel_tflops": kq, "out_kernel_tflops": w.out_flops() / (jo * 1e-3) / 1e12,
+                       "library_gemm_ms": lib,
+                       "library_gemm": "torch.matmul of the same operands (x w_qkv^T, o' w_o^T): plain GEMMs, "
+                                       "no rotation or head split"}
+        cfg["proj"]["qkv_kernel_ms_median"], cfg["proj"]["qkv_kernel_ms_min"] = med_min("jq")
+        line["roofline"] = {"bound": "mfma", "achieved": kq, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": kq / PEAK_BF16_TFLOPS, "traffic": traffic_for("proj_qkv", PROJ_SOURCES, w.name),
+                            "kernel": "proj_gemm_kernel<PROJ_QKV>"}
     if bwd:
         w = bwd.w
         bc, bk = avg("bc"), avg("bk")
@@ -604,6 +721,9 @@ def main():
         ok &= bool(torch.isfinite(dec8.out).all().item())
     if lat:
         ok &= bool(torch.isfinite(lat.out).all().item())
+    if pj:
+        for t in (pj.q, pj.k, pj.v, pj.y):
+            ok &= bool(torch.isfinite(t).all().item())
     if bwd:
         for t in (bwd.dq, bwd.dk, bwd.dv):
             ok &= bool(torch.isfinite(t).all().item())
@@ -633,7 +753,10 @@ def main():
                                      "prefill_kernel_vs_gemm": line["roofline"]["achieved"] / gemm}
         del a_, b_, c_
 
-    if not args.no_cpu_baseline and lat:
+    if not args.no_cpu_baseline and pj:
+        log("cpu baseline: timing the fp64 oracle projections on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_proj(pj, args.cpu_seqs_proj)
+    elif not args.no_cpu_baseline and lat:
         log("cpu baseline: timing the fp64 oracle latent decode on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline_latent(lat, args.cpu_seqs_latent)
     elif not args.no_cpu_baseline and dec8:
