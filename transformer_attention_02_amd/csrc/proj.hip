@@ -153,21 +153,19 @@ void proj_gemm_kernel(ProjArgs a) {
         wv[set][j] = *reinterpret_cast<const LDS bf16x8*>(lw + g_off(wn * 128 + 32 * j + n, 2 * s + hf));
     };
     load(0, 0);
+    // fenced order: the reads of step s+1, then the MFMAs of step s (whose
+    // operands were requested a whole step earlier); the block's last MFMAs
+    // stay ahead of the wait for the next block's DMA
 #pragma unroll
     for (int s = 0; s < GBK / 16; ++s) {
       if (s + 1 < GBK / 16) load(s + 1, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s & 1][i], wv[s & 1][j], acc[i][j], 0, 0, 0);
-      if (s + 1 < GBK / 16) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {  // one operand read after every two MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
