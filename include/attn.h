@@ -261,7 +261,8 @@ int attn_decode_fp8_fwd(const void* q, const void* k_new, const void* v_new, voi
 
 /*
  * Bytes of device workspace attn_decode_latent_fwd needs (folded queries,
- * split partials, merged latent outputs); 0 for non-positive sizes.
+ * split partials, merged latent outputs, the split kernel's work list); 0 for
+ * non-positive sizes.
  */
 size_t attn_decode_latent_workspace_bytes(int B, int H, int dc, int Lmax);
 

@@ -428,9 +428,10 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
 }  // namespace
 
 namespace {
-// Workspace of the latent decode: [folded queries bf16][partials fp32][(m, l)][merged latent outputs fp32].
+// Workspace of the latent decode: [folded queries bf16][partials fp32][(m, l)][merged latent outputs fp32]
+// [work list of the split kernel].
 struct LatentWs {
-  long long qt, part_o, part_ml, ot, total;
+  long long qt, part_o, part_ml, ot, items, total;
 };
 LatentWs latent_ws_layout(int B, int H, int dc, int Lmax) {
   auto up = [](long long x) { return (x + 255) / 256 * 256; };
@@ -441,7 +442,8 @@ LatentWs latent_ws_layout(int B, int H, int dc, int Lmax) {
   w.part_o = up(rows * dc * 2);
   w.part_ml = w.part_o + up(rows * nsplit * dc * 4);
   w.ot = w.part_ml + up(rows * nsplit * 8);
-  w.total = w.ot + up(rows * dc * 4);
+  w.items = w.ot + up(rows * dc * 4);
+  w.total = w.items + up(((long long)B * nsplit + 1) * 4);
   return w;
 }
 }  // namespace
@@ -495,6 +497,7 @@ int attn_decode_latent_fwd(const void* q, const void* c_new, void* c_cache, cons
   a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   a.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
   a.ot = reinterpret_cast<float*>(ws + lay.ot);
+  a.items = reinterpret_cast<int*>(ws + lay.items);
   a.B = B;
   a.H = H;
   a.hd = hd;

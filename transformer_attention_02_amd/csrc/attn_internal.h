@@ -87,6 +87,7 @@ struct LatentArgs {
   float* part_o;         // [B,H,nsplit,dc] (workspace)
   float2* part_ml;       // [B,H,nsplit]
   float* ot;             // [B,H,dc] merged latent outputs (workspace)
+  int* items;            // [B*nsplit + 1] (workspace): active (sequence, split) pairs, then their count
   int B, H, hd, dc, Lmax;
   int hblocks;           // ceil(H / 16)
   int split, nsplit;

@@ -62,9 +62,43 @@ __host__ __device__ constexpr int lat_off(int r, int c) { return r * DC * 2 + ((
 // operands come straight from memory in the MFMA layout: lane (n, g) of
 // k-step s holds dims 32s + 8g .. +7 of query row n (A) and of W_uk row n (B),
 // 16 contiguous bytes each, so all loads of a wave are in flight at once.
+// The split kernel's work list, built by one workgroup of the fold: the
+// active (sequence, split) pairs, sequence by sequence, as b * kLatentMaxSplits
+// + split, followed by their count. Split workgroup i takes pair i, so the
+// workgroups that do work are dispatched first and the surplus ones (the grid
+// is sized for every sequence at Lmax) exit at the end.
+__device__ void latent_build_items(const LatentArgs& a) {
+  __shared__ int part[256];
+  const int tid = threadIdx.x;
+  const int per = (a.B + 255) / 256;
+  const int b0 = min(a.B, tid * per), b1 = min(a.B, b0 + per);
+  auto nsplits = [&](int b) {
+    const int L = a.lens[b];
+    return lat_bad_len(L, a.Lmax) ? 0 : (L + 1 + a.split - 1) / a.split;
+  };
+  int cnt = 0;
+  for (int b = b0; b < b1; ++b) cnt += nsplits(b);
+  part[tid] = cnt;
+  __syncthreads();
+  // inclusive scan of the 256 counts (Hillis-Steele)
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int at = part[tid] - cnt;
+  for (int b = b0; b < b1; ++b) {
+    const int ns = nsplits(b);
+    for (int sp = 0; sp < ns; ++sp) a.items[at++] = b * kLatentMaxSplits + sp;
+  }
+  if (tid == 255) a.items[a.B * a.nsplit] = part[255];
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void latent_fold_kernel(LatentArgs a) {
   constexpr int NK = HD / 32;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) latent_build_items(a);
   const int h = blockIdx.x, lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int wave = threadIdx.x >> 6;
   const int b0 = blockIdx.y * 16, c0 = blockIdx.z * 64 + 16 * wave;
@@ -133,7 +167,11 @@ void latent_split_kernel(LatentArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int sp = blockIdx.y, hb = blockIdx.x % a.hblocks, b = blockIdx.x / a.hblocks;
+  // grid (B * nsplit, hblocks): workgroup i takes the i-th active (sequence, split) pair
+  const int nitems = a.items[a.B * a.nsplit];
+  if ((int)blockIdx.x >= nitems) return;
+  const int item = a.items[blockIdx.x];
+  const int b = item / kLatentMaxSplits, sp = item % kLatentMaxSplits, hb = blockIdx.y;
   const int L = a.lens[b];
   if (lat_bad_len(L, a.Lmax)) return;
   const int nk = L + 1;
@@ -164,6 +202,7 @@ void latent_split_kernel(LatentArgs a) {
   }
 
   const unsigned char* Cg = reinterpret_cast<const unsigned char*>(a.c_cache) + (long)b * a.Lmax * ROW;
+  // (The loads carry the non-temporal policy: the cache is read once per step.)
   // Wave w's part of tile t: rows 16w .. 16w+15, which only wave w reads, so
   // a wave waits for its own DMA and no barrier is needed while streaming.
   // Tiles of one split end before the next split starts; the descriptor ends
@@ -183,7 +222,7 @@ void latent_split_kernel(LatentArgs a) {
       const int p = 1024 * (wave * PW + i) + 16 * lane;
       const int row = p / ROW, pc = (p % ROW) / 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(stage + 1024 * (wave * PW + i)), 16,
-                                               row * ROW + ((pc ^ lat_swz(row)) << 4), 0, 0, 0);
+                                               row * ROW + ((pc ^ lat_swz(row)) << 4), 0, 0, 2);
     }
 #endif
   };
@@ -198,6 +237,24 @@ void latent_split_kernel(LatentArgs a) {
   const int trow = 16 * wave + 4 * g + (li >> 2);
   const int tcol = 4 * (li & 3);
   const int srow = 16 * wave + n;  // row read for S^T (natural key order)
+  // The swizzle is 4 bits, so a read's byte offset is a per-lane base that
+  // depends on the low bits of the chunk index plus 256 x the rest: row reads
+  // of chunk 4st + g use base sbase[st & 3] + 256 (st >> 2), transposing reads
+  // of dim block db use tbase[db & 7] + 256 (db >> 3) (instruction offsets).
+  int sbase[4], tbase[8];
+  {
+    const int sw = lat_swz(srow), tw = lat_swz(trow);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) sbase[m] = srow * ROW + 64 * (m ^ (sw >> 2)) + 16 * (g ^ (sw & 3));
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      tbase[m] = trow * ROW + 32 * (m ^ (tw >> 1)) + 16 * ((tcol >> 3) ^ (tw & 1)) + 2 * (tcol & 7);
+  }
+  static_assert(lat_off<512>(37, 4 * 9 + 2) == 37 * 1024 + 64 * (1 ^ (lat_swz(37) >> 2)) + 16 * (2 ^ (lat_swz(37) & 3)) + 256 * 2,
+                "row-read base decomposition");
+  static_assert(lat_off<512>(21, (16 * 11 + 8) >> 3) + 0 ==
+                    21 * 1024 + 32 * (3 ^ (lat_swz(21) >> 1)) + 16 * (1 ^ (lat_swz(21) & 1)) + 256 * 1,
+                "transposing-read base decomposition");
 
   f32x4 oacc[NB];
 #pragma unroll
@@ -216,7 +273,7 @@ void latent_split_kernel(LatentArgs a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NST - 1) * PW>());
     const int ts = k0 + t * LT;
     const int kw = ts + 16 * wave;  // the wave's first key
-    if (kw < nk) {
+    if (kw < k1) {
       LdsBytes tile = (LdsBytes)cur;
       if (own_slot && L >= kw && L < kw + 16 && lane < DC / 8) {
         const int r = L - ts;
@@ -225,7 +282,8 @@ void latent_split_kernel(LatentArgs a) {
       // S^T: every row read issued first, two independent accumulator chains
       bf16x8 av[NS];
 #pragma unroll
-      for (int st = 0; st < NS; ++st) av[st] = *reinterpret_cast<const LDS bf16x8*>(tile + lat_off<DC>(srow, 4 * st + g));
+      for (int st = 0; st < NS; ++st)
+        av[st] = *reinterpret_cast<const LDS bf16x8*>(tile + sbase[st & 3] + 256 * (st >> 2));
       f32x4 sa = f32x4{}, sb = f32x4{};
 #pragma unroll
       for (int st = 0; st < NS; st += 2) {
@@ -238,11 +296,9 @@ void latent_split_kernel(LatentArgs a) {
       // now so that they land under the softmax
       i16x4 tv[NB];
 #pragma unroll
-      for (int db = 0; db < NB; ++db) {
-        const int col = 16 * db + tcol;
+      for (int db = 0; db < NB; ++db)
         tv[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS i16x4*)((LDS unsigned char*)cur + lat_off<DC>(trow, col >> 3) + (col & 7) * 2));
-      }
+            (LDS i16x4*)((LDS unsigned char*)cur + tbase[db & 7] + 256 * (db >> 3)));
       const f32x4 s = sa + sb;
       // register i: key kw + 4g + i, column = head
       float x[4];
@@ -252,7 +308,7 @@ void latent_split_kernel(LatentArgs a) {
         const int key = kw + 4 * g + i;
         float v = s[i] * c2;
         if (a.alibi) v = fmaf(slope2, (float)(key - L), v);
-        v = key < nk ? v : -INFINITY;
+        v = key < k1 ? v : -INFINITY;
         x[i] = v;
         mx = fmaxf(mx, v);
       }
@@ -284,14 +340,17 @@ void latent_split_kernel(LatentArgs a) {
     // this wave's reads of the stage are done before its next DMA overwrites it
     __builtin_amdgcn_s_waitcnt(lgkm0_imm());
   };
-  // fully unrolled over the split's tiles (a loop back-edge would make the
-  // compiler's wait tracking of the in-flight stages conservative)
-  unroll_steps<0, kLatentSplit / LT>([&](auto tc) __attribute__((always_inline)) {
-    constexpr int T = decltype(tc)::value;
-    if (T >= ntile) return false;
-    step(T, std::integral_constant<int, T % NST>{});
-    return true;
-  });
+  // NST steps per iteration, so each names its stage statically. A step past
+  // the split's last tile finds an empty tile and computes nothing
+  // (its keys are at or past the split end k1); its DMA reads no memory. The
+  // loop keeps the code small: fully unrolled over a split, the kernel was
+  // about ten times the instruction cache and ran fetch-bound.
+  for (int t = 0; t < ntile; t += NST) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+    if constexpr (NST > 2) step(t + 2, std::integral_constant<int, 2>{});
+    if constexpr (NST > 3) step(t + 3, std::integral_constant<int, 3>{});
+  }
   __builtin_amdgcn_s_waitcnt(0);  // the empty tail tiles issued past the end
 
   float l_col = l_run + __shfl_xor(l_run, 16);
@@ -412,52 +471,75 @@ __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
 }
 
 // ------------------------------------------------------------------- 4. up
-// Grid (H, hd/32, ceil(B/8)), 256 threads: out[b, h, j] = sum_c o~[b, h, c]
-// W_uv[h][c][j] for 32 output dims j and 8 batch rows; thread (j, slice)
-// sums one eighth of the latent dims (the 8 rows of o~ transposed in LDS, one
-// pair of 16-byte reads per c), then the eight slices are added through LDS.
+// out[b, h, j] = sum_c o~[b, h, c] W_uv[h][c][j] on the fp32 matrix core
+// (v_mfma_f32_16x16x4f32: the fp32 latents times the bf16 weights widened to
+// fp32, exact products, fp32 sums). Grid (H, ceil(B/16), hd/64), 4 waves: the
+// workgroup owns 16 batch rows x 64 output dims of head h, wave w sums the
+// latent dims [w DC/4, (w+1) DC/4) and the four partial tiles add through LDS.
+// The order of the sum is free, so the operands are laid out for contiguous
+// loads: in step s lane group g takes latent dim c = cw + NST*g + s (a lane's
+// o~ values are one contiguous run), and column n of MFMA block jb is output
+// dim 4n + jb (a lane's 4 weights of a step are 8 contiguous bytes).
 template <int HD, int DC>
 __global__ __launch_bounds__(256) void latent_up_kernel(LatentArgs a) {
-  const int h = blockIdx.x, jj = threadIdx.x & 31, cs = threadIdx.x >> 5;
-  const int j = blockIdx.y * 32 + jj, b0 = blockIdx.z * 8;
-  constexpr int CS = DC / 8;  // latent dims per slice
-  __shared__ __attribute__((aligned(16))) float os[DC][8];
-  __shared__ float part[8][8][33];
+  constexpr int CW = DC / 4;    // latent dims per wave
+  constexpr int NST = CW / 4;   // MFMA steps per wave (4 dims each, one per lane group)
+  const int h = blockIdx.x, b0 = blockIdx.y * 16, j0 = blockIdx.z * 64;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int wave = tid >> 6;
+  const int c0 = wave * CW + NST * g;  // this lane's first latent dim
+  const bool row_ok = b0 + n < a.B;
+  // A operand: o~[b0 + n, h, c0 .. c0 + NST - 1] (zeros for rows past B)
+  // (a row past B reads row B-1 and is zeroed after the load: no branch, so
+  // every load of the lane is in flight before the first MFMA waits)
+  float4 a4[NST / 4];
+  {
+    const float4* src = reinterpret_cast<const float4*>(a.ot + ((long)min(b0 + n, a.B - 1) * a.H + h) * DC + c0);
 #pragma unroll
-  for (int e = threadIdx.x; e < 8 * DC; e += 256) {
-    const int r = e / DC, c = e % DC;
-    os[c][r] = (b0 + r < a.B) ? a.ot[((long)(b0 + r) * a.H + h) * DC + c] : 0.f;
+    for (int k = 0; k < NST / 4; ++k) a4[k] = src[k];
   }
-  __syncthreads();
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const uint16_t* w = reinterpret_cast<const uint16_t*>(a.w_uv) + ((long)h * DC + cs * CS) * HD + j;
-#pragma unroll 32
-  for (int c = 0; c < CS; ++c) {
-    const float wv = bf16_bits_to_f32(w[(long)c * HD]);
-    const float4 lo = *reinterpret_cast<const float4*>(&os[cs * CS + c][0]);
-    const float4 hi = *reinterpret_cast<const float4*>(&os[cs * CS + c][4]);
-    acc[0] = fmaf(wv, lo.x, acc[0]);
-    acc[1] = fmaf(wv, lo.y, acc[1]);
-    acc[2] = fmaf(wv, lo.z, acc[2]);
-    acc[3] = fmaf(wv, lo.w, acc[3]);
-    acc[4] = fmaf(wv, hi.x, acc[4]);
-    acc[5] = fmaf(wv, hi.y, acc[5]);
-    acc[6] = fmaf(wv, hi.z, acc[6]);
-    acc[7] = fmaf(wv, hi.w, acc[7]);
+  // B operand: W_uv[h][c0 + s][j0 + 4n .. + 3], 8 bytes per step
+  uint2 wv[NST];
+  {
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(a.w_uv) + ((long)h * DC + c0) * HD + j0 + 4 * n;
+#pragma unroll
+    for (int s = 0; s < NST; ++s) wv[s] = *reinterpret_cast<const uint2*>(w + (long)s * HD);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  float av[NST];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) part[cs][r][jj] = acc[r];
+  for (int k = 0; k < NST / 4; ++k) {
+    av[4 * k] = row_ok ? a4[k].x : 0.f;
+    av[4 * k + 1] = row_ok ? a4[k].y : 0.f;
+    av[4 * k + 2] = row_ok ? a4[k].z : 0.f;
+    av[4 * k + 3] = row_ok ? a4[k].w : 0.f;
+  }
+  f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+    const float wf[4] = {bf16_bits_to_f32(wv[s].x & 0xffffu), bf16_bits_to_f32(wv[s].x >> 16),
+                         bf16_bits_to_f32(wv[s].y & 0xffffu), bf16_bits_to_f32(wv[s].y >> 16)};
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) acc[jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], wf[jb], acc[jb], 0, 0, 0);
+  }
+  // lane (n, g) holds rows 4g + r, output dims 4n + jb: add the 4 waves' tiles
+  __shared__ float red[4][16][65];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][4 * g + r][4 * n + jb] = acc[jb][r];
   __syncthreads();
-  const int r = cs;  // 256 threads: (row r, dim jj)
-  if (b0 + r >= a.B) return;
-  float sum = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) sum += part[k][r][jj];
-  const long o = ((long)(b0 + r) * a.H + h) * HD + j;
-  if (a.out_bf16) {
-    reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16_bits(sum);
-  } else {
-    reinterpret_cast<float*>(a.out)[o] = sum;
+  for (int e = tid; e < 16 * 64; e += 256) {
+    const int r = e >> 6, j = e & 63;
+    if (b0 + r >= a.B) continue;
+    const float sum = red[0][r][j] + red[1][r][j] + red[2][r][j] + red[3][r][j];
+    const long o = ((long)(b0 + r) * a.H + h) * HD + j0 + j;
+    if (a.out_bf16) {
+      reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16_bits(sum);
+    } else {
+      reinterpret_cast<float*>(a.out)[o] = sum;
+    }
   }
 }
 
@@ -467,12 +549,12 @@ hipError_t launch_latent_hd(const LatentArgs& a, hipStream_t s, const TimingHook
   hipLaunchKernelGGL((latent_fold_kernel<HD>), dim3(a.H, (a.B + 15) / 16, DC / 64), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = tm.before(s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((latent_split_kernel<DC, kLW, kNST>), dim3(a.B * a.hblocks, a.nsplit), dim3(kLW * 64), 0, s, a);
+  hipLaunchKernelGGL((latent_split_kernel<DC, kLW, kNST>), dim3(a.B * a.nsplit, a.hblocks), dim3(kLW * 64), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = tm.after(s)) != hipSuccess) return e;
   hipLaunchKernelGGL((latent_merge_kernel<DC>), dim3(a.H, a.B), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((latent_up_kernel<HD, DC>), dim3(a.H, HD / 32, (a.B + 7) / 8), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((latent_up_kernel<HD, DC>), dim3(a.H, (a.B + 15) / 16, HD / 64), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

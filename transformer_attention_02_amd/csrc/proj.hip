@@ -121,16 +121,28 @@ void proj_gemm_kernel(ProjArgs a) {
   static_assert(g_off(9, 3) == 9 * 128 + ((3 ^ 4) << 4), "the DMA swizzle above is k_off<64>'s");
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.a, (int)a.a_bytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (int)a.w_bytes);
-  auto issue = [&](int kb, unsigned char* sa, unsigned char* sw) __attribute__((always_inline)) {
-    const unsigned ka = a_k_off<MODE>(a, kb), kw = (unsigned)(kb * GBK * 2);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.a, 0);  // empty: reads nothing, writes zeros
+  // Instructions 2s, 2s+1 of each operand slice of block kb (of GPW = 8 per
+  // wave), so a block's DMA goes out in four parts between its MFMAs. Past the
+  // last block the descriptors are empty: the loads read no memory and write
+  // zeros into the stage the finished block before it used.
+  auto issue_part = [&](int kb, unsigned char* sa, unsigned char* sw, int part) __attribute__((always_inline)) {
+    const bool live = kb < a.K / GBK;
+    const unsigned ka = live ? a_k_off<MODE>(a, kb) : 0u, kw = live ? (unsigned)(kb * GBK * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t qa = live ? ra : rz, qw = live ? rw : rz;
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS void*)(sa + 1024 * (wave * GPW + i)), 16, aoff[i], ka, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS void*)(sw + 1024 * (wave * GPW + i)), 16, woff[i], kw, 0, 0);
+    for (int i = 2 * part; i < 2 * part + 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qa, (LDS void*)(sa + 1024 * (wave * GPW + i)), 16, aoff[i], ka, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qw, (LDS void*)(sw + 1024 * (wave * GPW + i)), 16, woff[i], kw, 0, 0);
     }
 #endif
   };
+  auto issue = [&](int kb, unsigned char* sa, unsigned char* sw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int part = 0; part < GPW / 2; ++part) issue_part(kb, sa, sw, part);
+  };
+  static_assert(GPW == 2 * (GBK / 16), "two instructions per operand slice per 16-deep step");
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -140,8 +152,12 @@ void proj_gemm_kernel(ProjArgs a) {
 
   const int n = lane & 31, hf = lane >> 5;
   // one 64-wide K block: 4 steps of 16, each 4 A and 4 W operand reads and 16
-  // MFMAs; the reads of step s+1 go out between the MFMAs of step s
-  auto multiply = [&](const unsigned char* sa, const unsigned char* sw) __attribute__((always_inline)) {
+  // MFMAs. Fenced order per step: the operand reads of step s+1, then the 16
+  // MFMAs of step s (whose operands were requested a whole step earlier) with
+  // one LDS-DMA instruction of the next block after every four of them, so the
+  // DMA issue never holds the matrix core up in a burst.
+  auto multiply = [&](const unsigned char* sa, const unsigned char* sw, unsigned char* na, unsigned char* nw,
+                      int kn) __attribute__((always_inline)) {
     LdsBytes la = (LdsBytes)sa, lw = (LdsBytes)sw;
     bf16x8 av[2][4], wv[2][4];
     auto load = [&](int s, int set) __attribute__((always_inline)) {
@@ -153,18 +169,22 @@ void proj_gemm_kernel(ProjArgs a) {
         wv[set][j] = *reinterpret_cast<const LDS bf16x8*>(lw + g_off(wn * 128 + 32 * j + n, 2 * s + hf));
     };
     load(0, 0);
-    // fenced order: the reads of step s+1, then the MFMAs of step s (whose
-    // operands were requested a whole step earlier); the block's last MFMAs
-    // stay ahead of the wait for the next block's DMA
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < GBK / 16; ++s) {
       if (s + 1 < GBK / 16) load(s + 1, (s + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
+      issue_part(kn, na, nw, s);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s & 1][i], wv[s & 1][j], acc[i][j], 0, 0, 0);
+      if (s + 1 < GBK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -173,14 +193,14 @@ void proj_gemm_kernel(ProjArgs a) {
   issue(0, smem, smem + GTILE);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // Step: issue block kb+1 into the other stage (released by the barrier that
-  // ended the previous step), multiply block kb, wait for this wave's DMA and
-  // meet the others (block kb+1 is then complete and block kb's stage free).
+  // Step: multiply block kb while its DMA parts bring block kb+1 into the
+  // other stage (released by the barrier that ended the previous step), wait
+  // for this wave's DMA and meet the others (block kb+1 is then complete and
+  // block kb's stage free).
   for (int kb = 0; kb < nk; ++kb) {
     unsigned char* cur = smem + (kb & 1) * 2 * GTILE;
     unsigned char* nxt = smem + ((kb + 1) & 1) * 2 * GTILE;
-    if (kb + 1 < nk) issue(kb + 1, nxt, nxt + GTILE);
-    multiply(cur, cur + GTILE);
+    multiply(cur, cur + GTILE, nxt, nxt + GTILE, kb + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
