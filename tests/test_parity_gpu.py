@@ -583,6 +583,25 @@ def test_incremental_decode_equals_prefill():
     assert np.abs(to64(inc) - ref).max() <= 1e-2
 
 
+@pytest.mark.parametrize("dtype,hd", [("bf16", 128), ("f32", 64)])
+def test_decode_without_append_equals_append(dtype, hd):
+    """k_new = v_new = NULL: slot L already holds the new token. A step that appends, then the same
+    step over the cache it left with nothing to append, give bitwise the same output and lse (the
+    matrix-core kernel for bf16, the vector-ALU kernels for fp32), and the second leaves the cache alone."""
+    w = W.DecodeWorkload("decode-noappend", 5, 8, 2, hd, 0, 0, 5, 91, 10000.0, dtype=dtype)
+    lens = np.array([0, 1, 255, 700, 1500], dtype=np.int32)
+    inp = W.decode_inputs(w, lens=lens, lmax=1501)
+    out1, lse1, kc, vc = gpu_decode(inp, 10000.0, alibi=1)
+    k_after, v_after = kc.clone(), vc.clone()
+    out2 = torch.full_like(out1, float("nan"))
+    lse2 = torch.full_like(lse1, float("nan"))
+    bd.decode(inp.q.cuda(), None, None, kc, vc, torch.from_numpy(lens).cuda(), rope_base=10000.0, alibi=1,
+              out=out2, lse=lse2, out_dtype=out1.dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    assert torch.equal(kc, k_after) and torch.equal(vc, v_after)
+
+
 def test_decode_bad_length_gives_nan_not_a_fault():
     w = W.DecodeWorkload("decode-bad", 3, 4, 2, 64, 0, 0, 5, 43, 10000.0)
     lens = np.array([5, 9, 2], dtype=np.int32)

@@ -134,15 +134,6 @@ constexpr int vmcnt_imm() {
   return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
 }
 
-// f(integral_constant<T>) for T = T0 .. T1-1 in order, while it returns true.
-template <int T0, int T1, class F>
-__device__ __forceinline__ void unroll_steps(F&& f) {
-  if constexpr (T0 < T1) {
-    if (!f(std::integral_constant<int, T0>{})) return;
-    unroll_steps<T0 + 1, T1>(f);
-  }
-}
-
 constexpr int lgkm0_imm() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }  // lgkmcnt(0) only
 
 template <int DC, int LW, int NST>
