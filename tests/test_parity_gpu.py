@@ -551,6 +551,22 @@ def test_decode_latent_full_size_sampled():
     assert np.abs(to64(lse[pick]) - ref_lse).max() <= 2e-2
 
 
+def test_decode_latent_most_splits():
+    """The longest sequence the latent path takes: L = 262143 (Lmax = 262144), 512 splits of 512 keys
+    for the merge to combine, next to a short one; one head (hd 64, d_c 256) so the oracle's explicit
+    keys and values stay cheap."""
+    w = W.LatentDecodeWorkload("latent-longest", 2, 1, 64, 256, 0, 0, 5, 83)
+    lens = np.array([262143, 9], dtype=np.int32)
+    inp = W.latent_decode_inputs(w, lens=lens, lmax=262144)
+    print(f"[latent decode] most splits: lens={lens.tolist()}", flush=True)
+    out, lse, cc = gpu_decode_latent(inp)
+    ref, ref_lse, c_slot = attention_decode_latent(to64(inp.q), to64(inp.c_new), to64(inp.c_cache), lens,
+                                                   to64(inp.w_uk), to64(inp.w_uv))
+    assert np.abs(to64(out) - ref).max() <= 1e-2
+    assert np.abs(to64(lse) - ref_lse).max() <= 2e-2
+    assert np.array_equal(to64(cc[0, 262143]), c_slot[0])
+
+
 def test_decode_latent_bad_length_gives_nan():
     w = W.LatentDecodeWorkload("latent-bad", 3, 16, 128, 512, 0, 0, 5, 81)
     lens = np.array([5, 300, 20], dtype=np.int32)

@@ -196,3 +196,34 @@ def test_decode_step_with_projected_cache():
         L = int(lens[b])
         assert_bf16_close(to64(kc[b, :, L].cpu()), ref_k[b], f"k slot of {b}")
         assert_bf16_close(to64(vc[b, :, L].cpu()), ref_v[b], f"v slot of {b}")
+
+
+def test_proj_largest_operands():
+    """Operands just under the 2 GiB that one buffer descriptor spans: x [1, 1048575, 1024] (2 GiB less
+    2 KiB) through the QKV projection, and o [1, 8, 1048575, 128] (its head-gather offsets reach 1.9 GB)
+    through the output projection; rows near the end (the largest offsets) and at the start, every
+    column. Inputs drawn on the device from a seeded generator; the oracle sees the sampled rows."""
+    B, T, D, H, KV, hd = 1, 1048575, 1024, 8, 8, 128
+    print(f"[proj largest operands] T={T} D={D}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(61)
+    x = torch.randn(B, T, D, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn((H + 2 * KV) * hd, D, device="cuda", generator=g) / np.sqrt(D)).to(torch.bfloat16)
+    q, k, v = bd.qkv_proj(x, w, H, KV, pos0=0, rope_base=10000.0)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, T // 2, T - 257, T - 256, T - 2, T - 1]
+    w64 = to64(w)
+    for t in rows:
+        rq, rk, rv = qkv_projection(to64(x[:, t:t + 1]), w64, H=H, KV=KV, hd=hd, pos0=t, rope_base=10000.0)
+        assert_bf16_close(q[0, :, t], rq[0, :, 0], f"q row {t}")
+        assert_bf16_close(k[0, :, t], rk[0, :, 0], f"k row {t}")
+        assert_bf16_close(v[0, :, t], rv[0, :, 0], f"v row {t}")
+    del x, k, v
+    o = q  # [1, 8, T, 128] bf16, 2 GiB less 2 KiB
+    wo = (torch.randn(64, H * hd, device="cuda", generator=g) / np.sqrt(H * hd)).to(torch.bfloat16)
+    y = bd.out_proj(o, wo, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    wo64 = to64(wo)
+    for t in rows:
+        ry = out_projection(to64(o[:, :, t:t + 1]), wo64)
+        got = to64(y[0, t])
+        assert (np.abs(got - ry[0, 0]) <= 1e-5 * np.abs(ry[0, 0]) + 1e-4).all(), f"y row {t}"
