@@ -37,8 +37,14 @@ pair, ``roofline`` covers the QKV kernel, and the same two GEMMs through
 torch.matmul (the vendor library, without the epilogue work) are timed in the
 same run as context.
 
+``--workload block`` times the whole attention block of that page's module on
+the Llama-3-8B shape: the QKV projection with RoPE, causal GQA attention (the
+rotation off: q and k arrive rotated) and the output projection; ``value`` =
+TFLOP/s of the block (projections + attention), tokens per second in
+``config``, ``roofline`` for the block's longest kernel.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload all|prefill|decode|decode-fp8|latent-decode|proj|alibi|small|window|chunk|backward|copy]
+                       [--workload all|prefill|decode|decode-fp8|latent-decode|proj|block|alibi|small|window|chunk|backward|copy]
                        [--no-cpu-baseline] [--no-ceilings]
 """
 from __future__ import annotations
@@ -288,6 +294,49 @@ class Proj:
         return out
 
 
+class Block:
+    """The attention block: attn_qkv_proj_fwd (RoPE, head split), attn_prefill_fwd (causal, rotation off),
+    attn_out_proj_fwd, on the Llama-3-8B shape (inputs resident); each kernel timed."""
+
+    def __init__(self, dev, bd, W, torch):
+        self.pw, self.aw, self.bd = W.PROJ_LLAMA3_8B, W.LLAMA3_8B, bd
+        pw = self.pw
+        inp = W.proj_inputs(pw)
+        self.x, self.wq, self.wo = inp.x.to(dev), inp.w_qkv.to(dev), inp.w_o.to(dev)
+        bf = torch.bfloat16
+        self.q = torch.empty(pw.B, pw.H, pw.T, pw.hd, dtype=bf, device=dev)
+        self.k = torch.empty(pw.B, pw.KV, pw.T, pw.hd, dtype=bf, device=dev)
+        self.v = torch.empty(pw.B, pw.KV, pw.T, pw.hd, dtype=bf, device=dev)
+        self.o = torch.empty(pw.B, pw.H, pw.T, pw.hd, dtype=bf, device=dev)
+        self.y = torch.empty(pw.B, pw.T, pw.D, dtype=bf, device=dev)
+
+    def flops(self):
+        return self.pw.qkv_flops() + self.aw.flops() + self.pw.out_flops()
+
+    def __call__(self, stream, ev_qkv=None, ev_attn=None, ev_out=None):
+        pw, bd = self.pw, self.bd
+        if ev_qkv:
+            bd.attn_set_timing_events(*ev_qkv)
+        st = bd.attn_qkv_proj_fwd(self.x.data_ptr(), self.wq.data_ptr(), self.q.data_ptr(), self.k.data_ptr(),
+                                  self.v.data_ptr(), pw.B, pw.T, pw.D, pw.H, pw.KV, pw.hd, 0, pw.rope_base,
+                                  bd.ATTN_DTYPE_BF16, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_qkv_proj_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+        if ev_attn:
+            bd.attn_set_timing_events(*ev_attn)
+        st = bd.attn_prefill_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(), None,
+                                 pw.B, pw.T, pw.H, pw.KV, pw.hd, 0, 0.0, 1, 0, bd.ATTN_DTYPE_BF16,
+                                 bd.ATTN_DTYPE_BF16, None, 0, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_prefill_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+        if ev_out:
+            bd.attn_set_timing_events(*ev_out)
+        st = bd.attn_out_proj_fwd(self.o.data_ptr(), self.wo.data_ptr(), self.y.data_ptr(), pw.B, pw.T, pw.H, pw.hd,
+                                  pw.D, bd.ATTN_DTYPE_BF16, bd.ATTN_DTYPE_BF16, stream)
+        if st != bd.ATTN_OK:
+            raise RuntimeError(f"attn_out_proj_fwd: {bd.attn_status_str(st)} {bd.attn_last_error()}")
+
+
 class Backward:
     """attn_prefill_bwd on the forward's own out/lse (computed once, untimed)."""
 
@@ -451,6 +500,32 @@ def cpu_baseline_proj(pj, seqs):
             "max_abs_err_vs_gpu_bf16": err}
 
 
+def cpu_baseline_block(blk, tokens):
+    """The fp64 oracle of the block (projection with RoPE, causal attention, output projection) on the first
+    tokens of sequence 0; with a causal mask those output rows depend on those tokens only, so they are
+    checked against the GPU's rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_prefill, out_projection, qkv_projection
+
+    pw = blk.pw
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    T = min(tokens, pw.T)
+    x, wq, wo = f64(blk.x[:1, :T]), f64(blk.wq), f64(blk.wo)
+    t0 = time.perf_counter()
+    q, k, v = qkv_projection(x, wq, H=pw.H, KV=pw.KV, hd=pw.hd, rope_base=pw.rope_base)
+    o, _ = attention_prefill(q, k, v, rope_base=0.0, causal=True)
+    y = out_projection(o, wo)
+    secs = time.perf_counter() - t0
+    flops = 2.0 * T * pw.N_qkv * pw.D + 4.0 * pw.H * pw.hd * T * (T + 1) / 2 + 2.0 * T * pw.D * pw.H * pw.hd
+    err = float(np.abs(f64(blk.y[:1, :T]) - y).max())
+    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": flops / secs / 1e12,
+            "unit": "TFLOP/s", "seconds": secs, "sample": f"the block on tokens 0..{T - 1} of sequence 0",
+            "max_abs_err_vs_gpu_bf16": err}
+
+
 def cpu_baseline_bwd(bwd, heads):
     """The fp64 oracle backward on a bounded sample: the first ``heads`` query
     heads (whole GQA groups) of batch 0, all rows."""
@@ -484,8 +559,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "prefill", "decode", "decode-fp8", "latent-decode", "proj", "alibi", "small",
-                             "window", "chunk", "backward", "copy"],
+                    choices=["all", "prefill", "decode", "decode-fp8", "latent-decode", "proj", "block", "alibi",
+                             "small", "window", "chunk", "backward", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -495,6 +570,7 @@ def main():
     ap.add_argument("--cpu-heads-bwd", type=int, default=16)
     ap.add_argument("--cpu-seqs-latent", type=int, default=8)
     ap.add_argument("--cpu-seqs-proj", type=int, default=4)
+    ap.add_argument("--cpu-tokens-block", type=int, default=4096)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -539,6 +615,7 @@ def main():
     dec8 = DecodeFp8(W.KV_DECODE_FP8, dev, bd, W, torch) if args.workload == "decode-fp8" else None
     lat = LatentDecode(W.LATENT_DECODE, dev, bd, W, torch) if args.workload == "latent-decode" else None
     pj = Proj(W.PROJ_LLAMA3_8B, dev, bd, W, torch) if args.workload == "proj" else None
+    blk = Block(dev, bd, W, torch) if args.workload == "block" else None
     stream = torch.cuda.current_stream().cuda_stream
     bwd = Backward(W.LLAMA3_8B, dev, bd, W, torch, stream) if args.workload == "backward" else None
     log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None} "
@@ -557,11 +634,13 @@ def main():
             lat(stream)
         if pj:
             pj(stream)
+        if blk:
+            blk(stream)
     torch.cuda.synchronize()
 
     K = args.steps
     ev = {k: [(hip.create(), hip.create()) for _ in range(K)] for k in ("pc", "pk", "dc", "dk", "bc", "bk", "ec", "ek", "lc", "lk",
-                                                                     "jc", "jq", "jo")}
+                                                                     "jc", "jq", "jo", "xc", "xq", "xa", "xo")}
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
@@ -582,6 +661,10 @@ def main():
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["jc"][i][0]), ctypes.c_void_p(stream))
             pj(stream, ev["jq"][i], ev["jo"][i])
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["jc"][i][1]), ctypes.c_void_p(stream))
+        if blk:
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["xc"][i][0]), ctypes.c_void_p(stream))
+            blk(stream, ev["xq"][i], ev["xa"][i], ev["xo"][i])
+            hip.hip.hipEventRecord(ctypes.c_void_p(ev["xc"][i][1]), ctypes.c_void_p(stream))
         if dec8:
             hip.hip.hipEventRecord(ctypes.c_void_p(ev["ec"][i][0]), ctypes.c_void_p(stream))
             dec8(stream, ev["ek"][i])
@@ -695,6 +778,27 @@ def main():
         line["roofline"] = {"bound": "mfma", "achieved": kq, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": kq / PEAK_BF16_TFLOPS, "traffic": traffic_for("proj_qkv", PROJ_SOURCES, w.name),
                             "kernel": "proj_gemm_kernel<PROJ_QKV>"}
+    if blk:
+        pw, aw = blk.pw, blk.aw
+        xc, xq, xa, xo = avg("xc"), avg("xq"), avg("xa"), avg("xo")
+        line.update(value=blk.flops() / (xc * 1e-3) / 1e12, unit="TFLOP/s",
+                    metric="attention block (QKV projection + RoPE, causal GQA attention, output projection) "
+                           "TFLOP/s, 1 GPU")
+        cfg["workload"] = "llama3-8b attention block B=4 T=4096 D=4096 H=32 KV=8 hd=128 rope=5e5"
+        parts = {"qkv": (xq, pw.qkv_flops(), "proj_gemm_kernel<PROJ_QKV>"),
+                 "attention": (xa, aw.flops(), "prefill_mfma_kernel<128>"),
+                 "out": (xo, pw.out_flops(), "proj_gemm_kernel<PROJ_OUT>")}
+        cfg["block"] = {"B": pw.B, "T": pw.T, "D": pw.D, "H": pw.H, "KV": pw.KV, "hd": pw.hd,
+                        "rope_base": pw.rope_base, "flops": blk.flops(), "call_ms": xc,
+                        "tokens_per_s": pw.B * pw.T / (xc * 1e-3),
+                        "kernels": {k: {"ms": v[0], "tflops": v[1] / (v[0] * 1e-3) / 1e12} for k, v in parts.items()}}
+        name = max(parts, key=lambda k: parts[k][0])
+        ms, fl, kern = parts[name]
+        kt = fl / (ms * 1e-3) / 1e12
+        traffic = traffic_for("proj_qkv", PROJ_SOURCES, pw.name) if name == "qkv" else (
+            traffic_for("proj_out", PROJ_SOURCES, pw.name) if name == "out" else None)
+        line["roofline"] = {"bound": "mfma", "achieved": kt, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": kt / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kern}
     if bwd:
         w = bwd.w
         bc, bk = avg("bc"), avg("bk")
@@ -724,6 +828,8 @@ def main():
     if pj:
         for t in (pj.q, pj.k, pj.v, pj.y):
             ok &= bool(torch.isfinite(t).all().item())
+    if blk:
+        ok &= bool(torch.isfinite(blk.y).all().item())
     if bwd:
         for t in (bwd.dq, bwd.dk, bwd.dv):
             ok &= bool(torch.isfinite(t).all().item())
@@ -753,7 +859,10 @@ def main():
                                      "prefill_kernel_vs_gemm": line["roofline"]["achieved"] / gemm}
         del a_, b_, c_
 
-    if not args.no_cpu_baseline and pj:
+    if not args.no_cpu_baseline and blk:
+        log("cpu baseline: timing the fp64 oracle block on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_block(blk, args.cpu_tokens_block)
+    elif not args.no_cpu_baseline and pj:
         log("cpu baseline: timing the fp64 oracle projections on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline_proj(pj, args.cpu_seqs_proj)
     elif not args.no_cpu_baseline and lat:
