@@ -402,6 +402,10 @@ struct DkvWave {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // lse and D
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
+      // From here to the chunk's last MFMA the wave runs its exp / dS work and
+      // the products that consume it at raised issue priority, ahead of a wave
+      // starting its S / dP products (measured: the backward call ~2% faster).
+      __builtin_amdgcn_s_setprio(1);
       // register i of block b is query q0 + 32c + 8g + 4b + i
       const int dbase = kk - (q0 + r0);  // key - query at j = 0
       const float dbf = (float)dbase;
@@ -447,6 +451,7 @@ struct DkvWave {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
 };
