@@ -217,6 +217,8 @@ size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax);
  *   The new token sits at position L: its query and key are rotated at L and
  *   the query attends slots 0..L inclusive (ALiBi distance L - j).
  *   workspace: at least attn_decode_workspace_bytes(B, H, KV, hd, Lmax) bytes.
+ *   Lmax may be at most 2^24 (16,777,216) slots (ATTN_ERR_SHAPE otherwise);
+ *   a (sequence, head) slab of the cache may exceed 2 GiB.
  *
  * k_new and v_new may both be NULL: slot L of every sequence then already
  * holds the new token's key (rotated) and value, as attn_qkv_proj_cache_fwd

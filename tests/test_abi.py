@@ -186,6 +186,9 @@ def _decode(**kw):
     (dict(cache_lens=0x60002), bd.ATTN_ERR_ALIGN),
     (dict(workspace=None), bd.ATTN_ERR_WORKSPACE),
     (dict(workspace_bytes=64), bd.ATTN_ERR_WORKSPACE),
+    # more cache slots than the split grid covers (2^24 is the documented limit)
+    (dict(B=1, H=4, KV=1, Lmax=(1 << 24) + 1, workspace_bytes=1 << 40), bd.ATTN_ERR_SHAPE),
+    (dict(B=1, H=4, KV=1, Lmax=0x7fffffff, workspace_bytes=1 << 40), bd.ATTN_ERR_SHAPE),
 ])
 def test_decode_validation(kw, code):
     st = _decode(**kw)
@@ -211,6 +214,7 @@ def _decode_fp8(**kw):
     (dict(hd=32), bd.ATTN_ERR_UNSUPPORTED),
     (dict(H=34, KV=2), bd.ATTN_ERR_UNSUPPORTED),   # 17 query heads per KV head
     (dict(workspace_bytes=64), bd.ATTN_ERR_WORKSPACE),
+    (dict(B=1, H=4, KV=1, Lmax=(1 << 24) + 64, workspace_bytes=1 << 40), bd.ATTN_ERR_SHAPE),
 ])
 def test_decode_fp8_validation(kw, code):
     st = _decode_fp8(**kw)

@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 import torch
 
+from brute import brute_attention
 from oracle import attention_decode, attention_decode_latent, fold_query
 
 
@@ -71,24 +72,18 @@ def test_zero_query_averages_the_latents():
 
 def test_latent_decode_is_the_lab_block_with_latent_projections():
     """The lab's attention written with the latent projections (no RoPE, as the fold needs):
-    the last token's row of a causal block over all tokens equals a decode step whose cache
-    holds the earlier tokens' latents."""
+    the last token's row of a causal block over all tokens, computed by the scalar brute force
+    on the explicit per-head keys and values, equals a decode step whose cache holds the
+    earlier tokens' latents."""
     rng = np.random.default_rng(0)
     T, d, H, dc = 6, 32, 4, 8
     hd = d // H
-    x = rng.normal(size=(T, d))
-    wq = rng.normal(size=(d, H * hd)) / np.sqrt(d)
-    w_dkv = rng.normal(size=(d, dc)) / np.sqrt(d)
-    w_uk = rng.normal(size=(H, dc, hd)) / np.sqrt(dc)
-    w_uv = rng.normal(size=(H, dc, hd)) / np.sqrt(dc)
-    c = x @ w_dkv                                                 # [T, dc]
+    x, wq, w_dkv, w_uk, w_uv = (rng.normal(size=shape) / np.sqrt(fan_in) for shape, fan_in in (
+        ((T, d), 1.0), ((d, H * hd), d), ((d, dc), d), ((H, dc, hd), dc), ((H, dc, hd), dc)))
+    c = x @ w_dkv                                                 # latents [T, dc]
     q = (x @ wq).reshape(T, H, hd).transpose(1, 0, 2)              # [H, T, hd]
-    k = np.einsum("tc,hcd->htd", c, w_uk)
-    v = np.einsum("tc,hcd->htd", c, w_uv)
-    S = q @ k.transpose(0, 2, 1) / np.sqrt(hd)
-    S = np.where(np.tri(T)[None] > 0, S, -np.inf)
-    P = np.exp(S - S.max(-1, keepdims=True))
-    P /= P.sum(-1, keepdims=True)
-    full = P @ v                                                  # [H, T, hd]
+    k = np.stack([c @ w_uk[h] for h in range(H)])                  # each head's keys and values
+    v = np.stack([c @ w_uv[h] for h in range(H)])
+    full, _ = brute_attention(q[None], k[None], v[None], 0, 0.0, True, 0)
     out, _, _ = attention_decode_latent(q[:, -1][None], c[-1][None], c[None, :-1], np.array([T - 1]), w_uk, w_uv)
-    assert np.abs(out[0] - full[:, -1]).max() <= 1e-13
+    assert np.abs(out[0] - full[0, :, -1]).max() <= 1e-13

@@ -349,13 +349,9 @@ def gpu_decode(inp: W.DecodeInputs, rope_base, alibi=0, out_dtype=torch.float32)
     return out, lse, kc, vc
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("alibi", [0, 1])
-def test_decode_ragged_lengths(dtype, alibi):
-    w = W.DecodeWorkload("decode-small", 6, 8, 2, 128, 0, 0, 5, 41, 10000.0, dtype=dtype)
-    lens = np.array([0, 1, 255, 256, 257, 700], dtype=np.int32)
-    inp = W.decode_inputs(w, lens=lens, lmax=702)
-    print(f"[decode] {dtype} alibi={alibi} lens={lens.tolist()}", flush=True)
+def check_decode_ragged(w, dtype, alibi, lens, lmax):
+    inp = W.decode_inputs(w, lens=lens, lmax=lmax)
+    print(f"[decode] {w.name} H={w.H} KV={w.KV} hd={w.hd} {dtype} alibi={alibi} lens={lens.tolist()}", flush=True)
     out, lse, kc, vc = gpu_decode(inp, w.rope_base, alibi)
     ref, ref_lse, ks, vs = attention_decode(to64(inp.q), to64(inp.k_new), to64(inp.v_new), to64(inp.k_cache),
                                             to64(inp.v_cache), lens, rope_base=w.rope_base, alibi=alibi)
@@ -369,6 +365,50 @@ def test_decode_ragged_lengths(dtype, alibi):
         assert np.array_equal(vc64[b, :, L], vs[b])
         assert np.array_equal(kc64[b, :, :L], to64(inp.k_cache)[b, :, :L])  # history untouched
         assert np.array_equal(kc64[b, :, L + 1:], to64(inp.k_cache)[b, :, L + 1:])
+
+
+RAGGED_LENS = np.array([0, 1, 255, 256, 257, 700], dtype=np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("alibi", [0, 1])
+def test_decode_ragged_lengths(dtype, alibi):
+    w = W.DecodeWorkload("decode-small", 6, 8, 2, 128, 0, 0, 5, 41, 10000.0, dtype=dtype)
+    check_decode_ragged(w, dtype, alibi, RAGGED_LENS, 702)
+
+
+@pytest.mark.parametrize("H,KV,hd", [(64, 2, 64), (8, 2, 32), (6, 3, 16)], ids=lambda x: str(x))
+@pytest.mark.parametrize("alibi", [0, 1])
+def test_decode_bf16_vector_alu_path(H, KV, hd, alibi):
+    """bf16 decode shapes the matrix-core split kernel does not take (more than 16
+    query heads per KV head; head dims below 64) run the vector-ALU append and split
+    kernels: the same checks as the ragged matrix-core case."""
+    w = W.DecodeWorkload("decode-bf16-valu", 6, H, KV, hd, 0, 0, 5, 43 + hd, 10000.0)
+    check_decode_ragged(w, "bf16", alibi, RAGGED_LENS, 702)
+
+
+@pytest.mark.timeout(900)
+def test_decode_cache_slab_over_2gib():
+    """One (sequence, KV head) slab of the cache larger than 2 GiB (2^23 + 100 cached
+    slots of 128 bf16 = 2 GiB + 25 KiB, plus the new token): every buffer descriptor
+    of the split kernel covers one tile, so keys at any offset are read. Output, lse
+    and the written slot against the oracle over all 2^23 + 101 keys."""
+    L0 = (1 << 23) + 100
+    lens = np.array([L0], dtype=np.int32)
+    w = W.DecodeWorkload("decode-2gib-slab", 1, 4, 1, 128, 0, 0, 5, 47, 10000.0)
+    print(f"[decode >2 GiB slab] L={L0} H=4 KV=1 hd=128 bf16", flush=True)
+    inp = W.decode_inputs(w, lens=lens, lmax=L0 + 1)
+    out, lse, kc, vc = gpu_decode(inp, w.rope_base, alibi=1)
+    slot_k, slot_v = to64(kc[0, :, L0]), to64(vc[0, :, L0])
+    del kc, vc
+    torch.cuda.empty_cache()
+    f32 = lambda t: t.float().numpy()  # noqa: E731  (the oracle widens to fp64 itself)
+    ref, ref_lse, ks, vs = attention_decode(to64(inp.q), to64(inp.k_new), to64(inp.v_new), f32(inp.k_cache),
+                                            f32(inp.v_cache), lens, rope_base=w.rope_base, alibi=1)
+    assert np.abs(to64(out) - ref).max() <= 1e-2
+    assert np.abs(to64(lse) - ref_lse).max() <= 2e-2
+    assert np.abs(slot_k - ks[0]).max() <= 2.0 ** -8 * max(1.0, np.abs(ks[0]).max())
+    assert np.array_equal(slot_v, vs[0])
 
 
 def test_decode_full_size_sampled():

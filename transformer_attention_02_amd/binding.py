@@ -211,6 +211,42 @@ def _check(status: int):
         raise AttnError(status, attn_last_error())
 
 
+def _require(tensors: dict, dtype=None, same_dtype=True):
+    """Check torch tensors before their raw pointers cross the C ABI.
+
+    The library sees only pointers and sizes, so a strided view or a tensor of
+    another dtype would be read with the wrong layout. ``tensors`` maps names
+    to tensors (None entries are skipped); every tensor must be contiguous, of
+    ``dtype`` when given, and (``same_dtype``) all of one dtype. Raises
+    ValueError / TypeError before any launch; :func:`_require_gpu` then checks
+    the device.
+    """
+    items = [(n, t) for n, t in tensors.items() if t is not None]
+    for n, t in items:
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous (got strides {tuple(t.stride())} for shape {tuple(t.shape)})")
+    for n, t in items:
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{n} must be {dtype} (got {t.dtype})")
+    if same_dtype and items:
+        d0 = items[0][1].dtype
+        for n, t in items[1:]:
+            if t.dtype != d0:
+                raise TypeError(f"{n} is {t.dtype} but {items[0][0]} is {d0}")
+
+
+def _require_gpu(*tensors):
+    """Every tensor (None skipped) must live on the GPU: checked last, after layout, dtype and shape."""
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"a {tuple(t.shape)} {t.dtype} operand must be a GPU tensor (got device {t.device})")
+
+
+def _require_shape(name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
 def _stream_ptr(stream):
     import torch
 
@@ -235,20 +271,27 @@ def prefill(q, k, v, *, pos0=0, rope_base=10000.0, causal=True, alibi=ATTN_ALIBI
     """
     import torch
 
-    assert q.is_cuda and k.is_cuda and v.is_cuda, "tensors must be on the GPU"
-    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    _require({"q": q, "k": k, "v": v})
     B, H, Tq, hd = q.shape
     KV, Tk = k.shape[1], k.shape[2]
+    _require_shape("k", k, (B, KV, Tk, hd))
+    _require_shape("v", v, (B, KV, Tk, hd))
     dt = _dtype_code(q)
     odt = torch.float32 if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(B, H, Tq, hd, dtype=odt, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, Tq, dtype=torch.float32, device=q.device)
+    _require({"out": out})
+    _require({"lse": lse}, dtype=torch.float32)
+    _require_shape("out", out, (B, H, Tq, hd))
+    _require_shape("lse", lse, (B, H, Tq))
     if workspace is None:
         workspace, nbytes = prefill_workspace(B, Tk, KV, hd, dt, rope_base, q.device)
     else:
+        _require({"workspace": workspace})
         nbytes = workspace.numel() * workspace.element_size()
+    _require_gpu(q, k, v, out, lse, workspace)
     lse_ptr = lse.data_ptr() if lse is not None else None
     if Tq == Tk and q_offset == 0 and window == 0:
         st = attn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, Tq, H, KV, hd,
@@ -268,8 +311,14 @@ def prefill_bwd(q, k, v, out, lse, dout, *, pos0=0, rope_base=10000.0, causal=Tr
     lse, and dout (same dtype as out). Returns (dq, dk, dv); ``grad_dtype`` defaults to fp32."""
     import torch
 
+    _require({"q": q, "k": k, "v": v})
+    _require({"out": out, "dout": dout})
+    _require({"lse": lse}, dtype=torch.float32)
     B, H, T, hd = q.shape
     KV = k.shape[1]
+    for n_, t_, shp in (("k", k, (B, KV, T, hd)), ("v", v, (B, KV, T, hd)), ("out", out, (B, H, T, hd)),
+                        ("dout", dout, (B, H, T, hd)), ("lse", lse, (B, H, T))):
+        _require_shape(n_, t_, shp)
     dt = _dtype_code(q)
     gdt = torch.float32 if grad_dtype is None else grad_dtype
     if dq is None:
@@ -278,10 +327,15 @@ def prefill_bwd(q, k, v, out, lse, dout, *, pos0=0, rope_base=10000.0, causal=Tr
         dk = torch.empty(B, KV, T, hd, dtype=gdt, device=q.device)
     if dv is None:
         dv = torch.empty(B, KV, T, hd, dtype=gdt, device=q.device)
+    _require({"dq": dq, "dk": dk, "dv": dv})
+    for n_, t_, shp in (("dq", dq, (B, H, T, hd)), ("dk", dk, (B, KV, T, hd)), ("dv", dv, (B, KV, T, hd))):
+        _require_shape(n_, t_, shp)
     if workspace is None:
         n = attn_prefill_bwd_workspace_bytes(B, T, H, KV, hd, dt, rope_base)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _require({"workspace": workspace})
     nbytes = workspace.numel() * workspace.element_size()
+    _require_gpu(q, k, v, out, lse, dout, dq, dk, dv, workspace)
     st = attn_prefill_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, T, H, KV, hd, pos0, rope_base, int(causal),
                           alibi, dt, _dtype_code(out), _dtype_code(dq), workspace.data_ptr(), nbytes,
@@ -297,6 +351,23 @@ def decode_workspace(B, H, KV, hd, Lmax, device):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
 
 
+def _decode_shapes(B, H, KV, hd, Lmax, k_new, v_new, k_cache, v_cache, cache_lens):
+    _require_shape("k_new", k_new, (B, KV, hd))
+    _require_shape("v_new", v_new, (B, KV, hd))
+    _require_shape("k_cache", k_cache, (B, KV, Lmax, hd))
+    _require_shape("v_cache", v_cache, (B, KV, Lmax, hd))
+    _require_shape("cache_lens", cache_lens, (B,))
+
+
+def _decode_outputs(out, lse, B, H, hd):
+    import torch
+
+    _require({"out": out})
+    _require({"lse": lse}, dtype=torch.float32)
+    _require_shape("out", out, (B, H, hd))
+    _require_shape("lse", lse, (B, H))
+
+
 def decode(q, k_new, v_new, k_cache, v_cache, cache_lens, *, rope_base=10000.0, alibi=ATTN_ALIBI_NONE,
            out_dtype=None, want_lse=True, out=None, lse=None, workspace=None, stream=None):
     """Run attn_decode_fwd on GPU torch tensors (see include/attn.h for shapes). Returns (out, lse).
@@ -304,19 +375,26 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_lens, *, rope_base=10000.0, 
     k_new = v_new = None: slot cache_lens[b] already holds the new token (see attn_qkv_proj_cache_fwd)."""
     import torch
 
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    _require({"q": q, "k_new": k_new, "v_new": v_new, "k_cache": k_cache, "v_cache": v_cache})
+    _require({"cache_lens": cache_lens}, dtype=torch.int32)
     B, H, hd = q.shape
     KV, Lmax = k_cache.shape[1], k_cache.shape[2]
-    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
+    _decode_shapes(B, H, KV, hd, Lmax, k_new, v_new, k_cache, v_cache, cache_lens)
     dt = _dtype_code(q)
     odt = torch.float32 if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(B, H, hd, dtype=odt, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _decode_outputs(out, lse, B, H, hd)
     if workspace is None:
         workspace, nbytes = decode_workspace(B, H, KV, hd, Lmax, q.device)
     else:
+        _require({"workspace": workspace})
         nbytes = workspace.numel() * workspace.element_size()
+    _require_gpu(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, workspace)
     st = attn_decode_fwd(q.data_ptr(), None if k_new is None else k_new.data_ptr(),
                          None if v_new is None else v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                          cache_lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
@@ -331,19 +409,24 @@ def decode_fp8(q, k_new, v_new, k_cache, v_cache, cache_lens, k_scale, v_scale, 
     """Run attn_decode_fp8_fwd: caches are uint8 tensors of E4M3 codes. Returns (out, lse)."""
     import torch
 
+    _require({"q": q, "k_new": k_new, "v_new": v_new})
+    _require({"k_cache": k_cache, "v_cache": v_cache}, dtype=torch.uint8)
+    _require({"cache_lens": cache_lens}, dtype=torch.int32)
     B, H, hd = q.shape
     KV, Lmax = k_cache.shape[1], k_cache.shape[2]
-    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
-    assert k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8
+    _decode_shapes(B, H, KV, hd, Lmax, k_new, v_new, k_cache, v_cache, cache_lens)
     odt = torch.float32 if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(B, H, hd, dtype=odt, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _decode_outputs(out, lse, B, H, hd)
     if workspace is None:
         workspace, nbytes = decode_workspace(B, H, KV, hd, Lmax, q.device)
     else:
+        _require({"workspace": workspace})
         nbytes = workspace.numel() * workspace.element_size()
+    _require_gpu(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, workspace)
     st = attn_decode_fp8_fwd(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
                              v_cache.data_ptr(), cache_lens.data_ptr(), out.data_ptr(),
                              lse.data_ptr() if lse is not None else None, B, H, KV, hd, Lmax, rope_base, alibi,
@@ -358,18 +441,25 @@ def decode_latent(q, c_new, c_cache, cache_lens, w_uk, w_uv, *, alibi=ATTN_ALIBI
     """Run attn_decode_latent_fwd on GPU torch tensors (bf16). Returns (out, lse)."""
     import torch
 
+    _require({"q": q, "c_new": c_new, "c_cache": c_cache, "w_uk": w_uk, "w_uv": w_uv})
+    _require({"cache_lens": cache_lens}, dtype=torch.int32)
     B, H, hd = q.shape
     Lmax, dc = c_cache.shape[1], c_cache.shape[2]
-    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
+    for n_, t_, shp in (("c_new", c_new, (B, dc)), ("c_cache", c_cache, (B, Lmax, dc)), ("w_uk", w_uk, (H, dc, hd)),
+                        ("w_uv", w_uv, (H, dc, hd)), ("cache_lens", cache_lens, (B,))):
+        _require_shape(n_, t_, shp)
     odt = torch.float32 if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(B, H, hd, dtype=odt, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    _decode_outputs(out, lse, B, H, hd)
     if workspace is None:
         n = attn_decode_latent_workspace_bytes(B, H, dc, Lmax)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _require({"workspace": workspace})
     nbytes = workspace.numel() * workspace.element_size()
+    _require_gpu(q, c_new, c_cache, cache_lens, w_uk, w_uv, out, lse, workspace)
     st = attn_decode_latent_fwd(q.data_ptr(), c_new.data_ptr(), c_cache.data_ptr(), cache_lens.data_ptr(),
                                 w_uk.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
                                 lse.data_ptr() if lse is not None else None, B, H, hd, dc, Lmax, alibi,
@@ -382,8 +472,11 @@ def qkv_proj(x, w_qkv, H, KV, *, pos0=0, rope_base=10000.0, stream=None):
     """attn_qkv_proj_fwd on GPU bf16 tensors x [B,T,D], w_qkv [(H+2KV)hd, D]. Returns (q, k, v)."""
     import torch
 
+    _require({"x": x, "w_qkv": w_qkv})
     B, T, D = x.shape
     hd = w_qkv.shape[0] // (H + 2 * KV)
+    _require_shape("w_qkv", w_qkv, ((H + 2 * KV) * hd, D))
+    _require_gpu(x, w_qkv)
     q = torch.empty(B, H, T, hd, dtype=torch.bfloat16, device=x.device)
     k = torch.empty(B, KV, T, hd, dtype=torch.bfloat16, device=x.device)
     v = torch.empty(B, KV, T, hd, dtype=torch.bfloat16, device=x.device)
@@ -397,9 +490,14 @@ def qkv_proj_cache(x, w_qkv, k_cache, v_cache, cache_lens, H, *, rope_base=10000
     """attn_qkv_proj_cache_fwd: k/v of the T new tokens go to slots cache_lens[b] + t. Returns q."""
     import torch
 
+    _require({"x": x, "w_qkv": w_qkv, "k_cache": k_cache, "v_cache": v_cache})
+    _require({"cache_lens": cache_lens}, dtype=torch.int32)
     B, T, D = x.shape
     KV, Lmax, hd = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
-    assert cache_lens.dtype == torch.int32 and cache_lens.is_cuda
+    for n_, t_, shp in (("w_qkv", w_qkv, ((H + 2 * KV) * hd, D)), ("v_cache", v_cache, (B, KV, Lmax, hd)),
+                        ("k_cache", k_cache, (B, KV, Lmax, hd)), ("cache_lens", cache_lens, (B,))):
+        _require_shape(n_, t_, shp)
+    _require_gpu(x, w_qkv, k_cache, v_cache, cache_lens)
     q = torch.empty(B, H, T, hd, dtype=torch.bfloat16, device=x.device)
     st = attn_qkv_proj_cache_fwd(x.data_ptr(), w_qkv.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                  cache_lens.data_ptr(), B, T, D, H, KV, hd, Lmax, rope_base, _dtype_code(x),
@@ -412,8 +510,11 @@ def out_proj(o, w_o, *, out_dtype=None, stream=None):
     """attn_out_proj_fwd on GPU tensors o [B,H,T,hd] bf16, w_o [D, H*hd] bf16. Returns y [B,T,D]."""
     import torch
 
+    _require({"o": o, "w_o": w_o})
     B, H, T, hd = o.shape
     D = w_o.shape[0]
+    _require_shape("w_o", w_o, (D, H * hd))
+    _require_gpu(o, w_o)
     y = torch.empty(B, T, D, dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=o.device)
     st = attn_out_proj_fwd(o.data_ptr(), w_o.data_ptr(), y.data_ptr(), B, T, H, hd, D, _dtype_code(o), _dtype_code(y),
                            _stream_ptr(stream))

@@ -372,6 +372,8 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
   if (H > 65535 || B > 65535 || KV > 65535) return fail(ATTN_ERR_SHAPE, "H, KV and B must be <= 65535");
   if (int c = check_common(dtype, out_dtype, alibi, rope_base, hd)) return c;
   if ((long long)B * KV * Lmax * hd > kMaxElems) return fail(ATTN_ERR_SHAPE, "cache too large");
+  // (the split grid holds at most 65535 splits per sequence)
+  if (Lmax > kMaxDecodeLmax) return fail(ATTN_ERR_SHAPE, "Lmax=%d exceeds %d cache slots", Lmax, kMaxDecodeLmax);
   if (!aligned(q, 16) || (append && (!aligned(k_new, 16) || !aligned(v_new, 16))) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(out, 16))
     return fail(ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");

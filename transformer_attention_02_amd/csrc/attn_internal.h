@@ -13,6 +13,7 @@ constexpr int kDecodeSplit = 256;  // keys per split-KV partial, vector-ALU deco
 constexpr int kSplitMfma = 512;    // keys per split-KV partial, MFMA decode kernel
 constexpr int kSplitMfmaLong = 1024;  // the same when the batch gives enough splits anyway
 constexpr int kSplitMfmaFp8 = 2048;   // fp8 cache: the same bytes per workgroup as the long bf16 split
+constexpr int kMaxDecodeLmax = 1 << 24;  // cache slots per sequence the decode entry points accept
 
 // 4 theta_i / (2 pi) in fp64 (quarter turns per position) for i = 0 .. hd/2-1,
 // theta_i = base^(-2i/hd).

@@ -238,16 +238,18 @@ void decode_split_mfma_kernel(DecodeArgs a) {
   // is written to LDS, then receives tile t + NSLOT. The first ones go out
   // before the rotary table and the query set-up, which then hide under their
   // latency.
-  // Buffer descriptors start at the tile and end at key slot nk, so rows past
-  // the sequence end read as zero. (The wave whose tile covers slot L may read
-  // it before the new key lands there; it patches that row in LDS.)
+  // Buffer descriptors start at the tile and end at key slot nk or at the
+  // tile's end, whichever comes first, so rows past the sequence end read as
+  // zero and the 32-bit descriptor size never exceeds one tile, however long
+  // the cache. (The wave whose tile covers slot L may read it before the new
+  // key lands there; it patches that row in LDS.)
   uint4 kr[NSLOT][LOADS], vr[NSLOT][LOADS];
   // Issued unconditionally (a tile at or past the sequence end gets an empty
   // descriptor: every lane reads zero and no memory is touched), so the wait
   // before each tile's LDS write counts only that tile's loads; a conditional
   // issue would make the compiler drain every load in flight there.
   auto load_tile = [&](int slot, int ts) {
-    const int bytes = max(nk - ts, 0) * HD * EB;
+    const int bytes = min(max(nk - ts, 0), kTile) * HD * EB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)ts * HD * EB, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)ts * HD * EB, bytes);
 #pragma unroll

@@ -198,15 +198,15 @@ def lab_instance():
 
     T=6 tokens, width d=32, H=4 query heads, KV=2 key/value heads, hd=8.
     """
-    rng = np.random.default_rng(0)
     T, d, H, KV = 6, 32, 4, 2
     hd = d // H
-    x = rng.normal(size=(T, d))
-    Wq = rng.normal(size=(d, H * hd)) / np.sqrt(d)
-    Wk = rng.normal(size=(d, KV * hd)) / np.sqrt(d)
-    Wv = rng.normal(size=(d, KV * hd)) / np.sqrt(d)
-    Wo = rng.normal(size=(H * hd, d)) / np.sqrt(d)
-    return x, Wq, Wk, Wv, Wo
+    # One generator seeded with 0 draws, in order, the tokens x (unscaled) and the
+    # query, key, value and output weights, each divided by sqrt(d): the page's
+    # draw order, which its two printed checks depend on.
+    draws = (((T, d), 1.0), ((d, H * hd), np.sqrt(d)), ((d, KV * hd), np.sqrt(d)), ((d, KV * hd), np.sqrt(d)),
+             ((H * hd, d), np.sqrt(d)))
+    rng = np.random.default_rng(0)
+    return tuple(rng.normal(size=shape) / div for shape, div in draws)
 
 
 def split_heads(y: np.ndarray, heads: int) -> np.ndarray:
