@@ -234,6 +234,28 @@ int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k
                     int dtype, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc. Arguments, results and kernels are those of
+ * attn_decode_fwd (outputs bitwise equal). The split partials live in a
+ * library-owned static device array of 32 MiB per GPU (created when the
+ * library's code is loaded on that GPU, held until the process ends); the
+ * stream must belong to the current device. The partials of one step take
+ * B * H * ceil(Lmax / split) * (hd * 4 + 8) bytes, rounded up to 256, where
+ * split is 256 slots on the vector-ALU path and 512 or 1024 on the
+ * matrix-core path (1024 when B * KV * ceil(Lmax / 1024) >= 1024); a step that
+ * needs more returns ATTN_ERR_WORKSPACE before any HIP call. (The 64-sequence,
+ * 8193-slot, 32-head, hd-128 step needs 8.5 MB.) Nothing is allocated, freed
+ * or cleared: every partial the merge reads is written first in the same
+ * call. Calls that overlap in time on one GPU (different streams or host
+ * threads) share the array and race; serialise them.
+ */
+int attn_decode_fwd_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* cache_lens, void* out, float* lse,
+                            int B, int H, int KV, int hd, int Lmax, double rope_base, int alibi,
+                            int dtype, int out_dtype, void* stream);
+
+/*
  * The same decode step over a cache held in 8-bit floats, the quantized
  * storage that "Build a Transformer Self-Attention Block from Scratch in Pure
  * Python" lists on its roadmap against the memory-bandwidth bottleneck (the

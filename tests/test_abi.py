@@ -350,3 +350,19 @@ def test_launch_without_a_device_reports_hip_error():
     assert _qkv() == bd.ATTN_ERR_HIP
     assert _qkv_cache() == bd.ATTN_ERR_HIP
     assert _outp(out_dtype=bd.ATTN_DTYPE_F32) == bd.ATTN_ERR_HIP
+
+
+def test_decode_noalloc_validation_runs_before_any_hip_call():
+    """The allocation-free decode validates like attn_decode_fwd, and refuses a step whose
+    partials exceed its 32 MiB array, before touching a GPU."""
+    args = dict(q=FAKE, k_new=FAKE2, v_new=FAKE3, k_cache=FAKE4, v_cache=0x50000, cache_lens=0x60000, out=0x70000,
+                lse=None, B=2, H=8, KV=2, hd=128, Lmax=1000, rope_base=10000.0, alibi=0, dtype=bd.ATTN_DTYPE_BF16,
+                out_dtype=bd.ATTN_DTYPE_F32, stream=None)
+    for kw, code in [(dict(q=None), bd.ATTN_ERR_NULL), (dict(H=8, KV=3), bd.ATTN_ERR_SHAPE),
+                     (dict(k_cache=FAKE4 + 4), bd.ATTN_ERR_ALIGN), (dict(Lmax=(1 << 24) + 1), bd.ATTN_ERR_SHAPE),
+                     # fp32: 256-slot splits, 128 * 64 * 32 * 520 bytes > 32 MiB
+                     (dict(B=128, H=64, KV=8, Lmax=8192, dtype=bd.ATTN_DTYPE_F32), bd.ATTN_ERR_WORKSPACE)]:
+        a = dict(args)
+        a.update(kw)
+        st = bd.attn_decode_fwd_noalloc(**a)
+        assert st == code, (kw, st, bd.attn_last_error())

@@ -44,6 +44,7 @@ EXPORTS = (
     "attn_prefill_bwd",
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
+    "attn_decode_fwd_noalloc",
     "attn_decode_fp8_fwd",
     "attn_decode_latent_workspace_bytes",
     "attn_decode_latent_fwd",
@@ -72,6 +73,7 @@ _SIGS = {
                               _S, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I, _P, _S, _P]),
+    "attn_decode_fwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _I, _I, _P]),
     "attn_decode_fp8_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _D, _I, _F, _F, _I, _I, _P, _S,
                                  _P]),
     "attn_decode_latent_workspace_bytes": (_S, [_I, _I, _I, _I]),
@@ -162,6 +164,12 @@ def attn_decode_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, 
                     dtype, out_dtype, workspace, workspace_bytes, stream) -> int:
     return load().attn_decode_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax,
                                   float(rope_base), alibi, dtype, out_dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_fwd_noalloc(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base,
+                            alibi, dtype, out_dtype, stream) -> int:
+    return load().attn_decode_fwd_noalloc(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax,
+                                          float(rope_base), alibi, dtype, out_dtype, stream)
 
 
 def attn_decode_fp8_fwd(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base, alibi,

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/attn.h"
@@ -335,13 +336,14 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* ou
 }
 
 namespace {
-// Workspace layout (sized for the smaller split, so it fits either kernel):
-// [part_o: rows*hd fp32][part_ml: rows float2], rows = B*H*ceil(Lmax/256).
+// Workspace layout: [part_o: rows*hd fp32][part_ml: rows float2], rows =
+// B*H*ceil(Lmax/split). The caller-owned workspace is sized for the smallest
+// split (256 slots), so it fits whichever kernel runs.
 struct DecodeWs {
   long long part_o, part_ml, total;
 };
-DecodeWs decode_ws_layout(int B, int H, int hd, int Lmax) {
-  const long long rows = (long long)B * H * ((Lmax + kDecodeSplit - 1) / kDecodeSplit);
+DecodeWs decode_ws_layout(int B, int H, int hd, int Lmax, int split = kDecodeSplit) {
+  const long long rows = (long long)B * H * ((Lmax + split - 1) / split);
   DecodeWs w;
   w.part_o = 0;
   w.part_ml = rows * hd * 4;
@@ -356,10 +358,42 @@ size_t attn_decode_workspace_bytes(int B, int H, int KV, int hd, int Lmax) {
 }
 
 namespace {
+// ---- scratch of the allocation-free decode entry point
+// The split partials of attn_decode_fwd_noalloc live in this file-scope device
+// array: one copy per GPU, created when the library's code object is loaded
+// on that GPU and held until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: its device address on the current
+// GPU comes from hipGetSymbolAddress, looked up once per device and kept.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (int c = hip_status(hipGetDevice(&dev), "hipGetDevice")) return c;
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_HIP, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (int c = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) return c;
+    if (!p) return fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// Shared body of the decode entry points. noalloc: the partials go to the
+// per-device scratch array instead of the caller's workspace.
 int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                 const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
                 double rope_base, int alibi, int dtype, int out_dtype, void* workspace, size_t workspace_bytes,
-                void* stream, int fp8, float k_scale, float v_scale) {
+                void* stream, int fp8, float k_scale, float v_scale, bool noalloc = false) {
   if (!q || !k_cache || !v_cache || !cache_lens || !out)
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, cache_lens and out must be non-NULL");
   // k_new and v_new both NULL: slot L already holds the new token (bf16/fp32 caches only)
@@ -379,10 +413,13 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
     return fail(ATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(cache_lens, 4) || (lse && !aligned(lse, 4)))
     return fail(ATTN_ERR_ALIGN, "cache_lens and lse must be 4-byte aligned");
-  const size_t need = attn_decode_workspace_bytes(B, H, KV, hd, Lmax);
-  if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes required", need);
-  if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
-  if (!aligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!noalloc) {
+    const size_t need = attn_decode_workspace_bytes(B, H, KV, hd, Lmax);
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
 
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
@@ -400,10 +437,20 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
   a.hd = hd;
   a.group = H / KV;
   a.Lmax = Lmax;
-  const DecodeWs lay = decode_ws_layout(B, H, hd, Lmax);
-  char* ws = reinterpret_cast<char*>(workspace);
-  a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
-  a.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
+  a.fp8 = fp8;
+  DecodeWs lay = decode_ws_layout(B, H, hd, Lmax);
+  if (noalloc) {
+    // sized for the split the launcher picks (checked before any HIP call)
+    lay = decode_ws_layout(B, H, hd, Lmax, decode_split_for(a, dtype == ATTN_DTYPE_BF16));
+    if ((unsigned long long)lay.total > kNoAllocScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE, "the step needs %lld bytes of partials; the allocation-free entry point holds %zu",
+                  lay.total, kNoAllocScratchBytes);
+  }
+  if (!noalloc) {
+    char* ws = reinterpret_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    a.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
+  }
   a.split = kDecodeSplit;  // the launcher sets the split of the kernel it picks
   a.nsplit = (Lmax + kDecodeSplit - 1) / kDecodeSplit;
   a.rope = rope_base != 0.0;
@@ -422,6 +469,13 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cac
     if (dtype != ATTN_DTYPE_BF16 || !decode_mfma_supported(a, 1))
       return fail(ATTN_ERR_UNSUPPORTED, "fp8 cache: bf16 q/k_new/v_new, hd 64 or 128 and H/KV <= 16 (got dtype %d, "
                                         "hd %d, H/KV %d)", dtype, hd, H / KV);
+  }
+  if (noalloc) {  // every argument is valid: now the one HIP call of the set-up
+    void* p = nullptr;
+    if (int c = scratch_ptr(&p)) return c;
+    char* ws = reinterpret_cast<char*>(p);
+    a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    a.part_ml = reinterpret_cast<float2*>(ws + lay.part_ml);
   }
   const TimingHook tm = take_timing();
   return hip_status(launch_decode(a, dtype == ATTN_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream), tm),
@@ -521,6 +575,13 @@ int attn_decode_fwd(const void* q, const void* k_new, const void* v_new, void* k
                     void* stream) {
   return decode_impl(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base, alibi,
                      dtype, out_dtype, workspace, workspace_bytes, stream, 0, 1.f, 1.f);
+}
+
+int attn_decode_fwd_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* cache_lens, void* out, float* lse, int B, int H, int KV, int hd, int Lmax,
+                            double rope_base, int alibi, int dtype, int out_dtype, void* stream) {
+  return decode_impl(q, k_new, v_new, k_cache, v_cache, cache_lens, out, lse, B, H, KV, hd, Lmax, rope_base, alibi,
+                     dtype, out_dtype, nullptr, 0, stream, 0, 1.f, 1.f, true);
 }
 
 int attn_decode_fp8_fwd(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

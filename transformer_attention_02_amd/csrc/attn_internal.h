@@ -142,6 +142,7 @@ bool prefill_mfma_supported(const PrefillArgs& a, int bf16);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s, const TimingHook& tm);
 bool decode_mfma_supported(const DecodeArgs& a, int bf16);
+int decode_split_for(const DecodeArgs& a, int bf16);  // key slots per split the launcher uses
 hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t s);
 hipError_t launch_bwd_valu(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkv_valu(const BwdArgs& a, hipStream_t s);

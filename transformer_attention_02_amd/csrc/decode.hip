@@ -535,6 +535,17 @@ bool decode_mfma_supported(const DecodeArgs& a, int bf16) {
   return bf16 && (a.hd == 64 || a.hd == 128) && a.group <= 16;
 }
 
+int decode_split_for(const DecodeArgs& a, int bf16) {
+  if (!decode_mfma_supported(a, bf16)) return kDecodeSplit;
+  // MFMA path: the longer split when it still gives at least four workgroups
+  // per CU (measured on the 64-sequence, 8-KV-head cache: 5.6 -> 6.0 TB/s), so
+  // the per-workgroup set-up is amortised over more keys.
+  const bool long_split = (long)a.KV * a.B * ((a.Lmax + kSplitMfmaLong - 1) / kSplitMfmaLong) >= 1024;
+  // fp8: half the bytes per key, so twice the keys per workgroup for the same set-up cost
+  const bool fp8_split = a.fp8 && (long)a.KV * a.B * ((a.Lmax + kSplitMfmaFp8 - 1) / kSplitMfmaFp8) >= 1024;
+  return fp8_split ? kSplitMfmaFp8 : (long_split ? kSplitMfmaLong : kSplitMfma);
+}
+
 namespace {
 
 template <int BF16, int HD>
@@ -542,13 +553,7 @@ hipError_t launch_decode_hd(const DecodeArgs& a0, hipStream_t s, const TimingHoo
   DecodeArgs a = a0;
   const bool mfma = decode_mfma_supported(a, BF16);
   if (a.fp8 && !mfma) return hipErrorInvalidValue;  // the host checks this first
-  // MFMA path: the longer split when it still gives at least four workgroups
-  // per CU (measured on the 64-sequence, 8-KV-head cache: 5.6 -> 6.0 TB/s), so
-  // the per-workgroup set-up is amortised over more keys.
-  const bool long_split = (long)a.KV * a.B * ((a.Lmax + kSplitMfmaLong - 1) / kSplitMfmaLong) >= 1024;
-  // fp8: half the bytes per key, so twice the keys per workgroup for the same set-up cost
-  const bool fp8_split = a.fp8 && (long)a.KV * a.B * ((a.Lmax + kSplitMfmaFp8 - 1) / kSplitMfmaFp8) >= 1024;
-  a.split = mfma ? (fp8_split ? kSplitMfmaFp8 : (long_split ? kSplitMfmaLong : kSplitMfma)) : kDecodeSplit;
+  a.split = decode_split_for(a, BF16);
   a.nsplit = (a.Lmax + a.split - 1) / a.split;
   hipError_t e = hipSuccess;
   if (!mfma && a.append) {  // the MFMA split kernel appends the new token itself
