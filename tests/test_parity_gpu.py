@@ -5,7 +5,7 @@ Tolerances (max absolute error of the output, fp32 output unless noted):
   * bf16 inputs: 1e-2 (inputs rounded to bf16 exactly as the oracle sees them;
     the kernel rounds rotated Q/K and the softmax weights to bf16 for the
     matrix cores and accumulates in fp32).
-  * log-sum-exp: 1e-5 (fp32) / 2e-2 (bf16).
+  * log-sum-exp: 1e-5 (fp32) / 1e-2 (bf16; measured at most 0.004 on the full Llama-3-8B prefill).
 Exact (bitwise) properties: causality and determinism.
 """
 import math
@@ -16,13 +16,14 @@ import torch
 
 from oracle import (attention_decode, attention_decode_fp8, attention_decode_latent, attention_prefill,
                     attention_prefill_bwd, e4m3_decode)
+from guards import Guarded, check_all
 from transformer_attention_02_amd import binding as bd
 from transformer_attention_02_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
-LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+LSE_TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 
 
 def to64(t):
@@ -30,14 +31,18 @@ def to64(t):
 
 
 def gpu_prefill(q, k, v, **kw):
+    """The prefill through the binding, with guard bands around out, lse and the workspace."""
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
     B, H, T, hd = q.shape
+    KV, Tk = k.shape[1], k.shape[2]
     odt = kw.pop("out_dtype", torch.float32)
-    out = torch.full((B, H, T, hd), float("nan"), dtype=odt, device="cuda")
-    lse = torch.full((B, H, T), float("nan"), dtype=torch.float32, device="cuda")
-    bd.prefill(dq, dk, dv, out=out, lse=lse, out_dtype=odt, **kw)
-    torch.cuda.synchronize()
-    return out, lse
+    out = Guarded((B, H, T, hd), odt)
+    lse = Guarded((B, H, T), torch.float32)
+    n = bd.attn_prefill_workspace_bytes(B, Tk, KV, hd, bd._dtype_code(dq), kw.get("rope_base", 10000.0))
+    ws = Guarded((max(n, 1),), torch.uint8, fill=0)
+    bd.prefill(dq, dk, dv, out=out.t, lse=lse.t, out_dtype=odt, workspace=ws.t, **kw)
+    check_all(out=out, lse=lse, workspace=ws)
+    return out.t, lse.t
 
 
 def check_prefill(q, k, v, pos0=0, rope_base=10000.0, causal=True, alibi=0, label="", q_offset=0, window=0):
@@ -175,8 +180,8 @@ def test_chunked_prefill_equals_full_prefill_bitwise():
 # fp32: fp32 accumulation over at most a few hundred terms. bf16: the matrix-core
 # kernels round the recomputed weights p and ds to bf16 (relative 2^-9 each) for
 # the products, and the forward's bf16-rounded inputs propagate; measured errors
-# sit well inside 2e-2 of the gradient scale.
-GRAD_TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+# are 0.2-0.5% of the gradient scale, so 1e-2 of it leaves a 2x margin.
+GRAD_TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
 
 BWD_SHAPES = [
     # B, T, H, KV, hd, causal, alibi, rope_base
@@ -198,9 +203,16 @@ def check_backward(q, k, v, dout, causal, alibi, base, label=""):
     print(f"[backward] {label} q{tuple(q.shape)} k{tuple(k.shape)} {q.dtype} causal={causal} alibi={alibi} "
           f"base={base}", flush=True)
     out, lse = gpu_prefill(q, k, v, rope_base=base, causal=causal, alibi=alibi, out_dtype=q.dtype)
+    B, H, T, hd = q.shape
+    KV = k.shape[1]
+    gq = Guarded((B, H, T, hd), torch.float32)
+    gk = Guarded((B, KV, T, hd), torch.float32)
+    gv = Guarded((B, KV, T, hd), torch.float32)
+    n = bd.attn_prefill_bwd_workspace_bytes(B, T, H, KV, hd, bd._dtype_code(q), base)
+    ws = Guarded((max(n, 1),), torch.uint8, fill=0)
     dq, dk, dv = bd.prefill_bwd(q.cuda(), k.cuda(), v.cuda(), out, lse, dout.cuda(), rope_base=base, causal=causal,
-                                alibi=alibi)
-    torch.cuda.synchronize()
+                                alibi=alibi, dq=gq.t, dk=gk.t, dv=gv.t, workspace=ws.t)
+    check_all(dq=gq, dk=gk, dv=gv, workspace=ws)
     rq, rk, rv = attention_prefill_bwd(to64(q), to64(k), to64(v), to64(dout), rope_base=base, causal=causal,
                                        alibi=alibi)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
@@ -305,48 +317,67 @@ def test_first_row_is_first_value():
     assert (out[0, :, 0].cpu() - expect).abs().max().item() <= 1e-6
 
 
-# --------------------------------------------------- full-size sampled rows
-def sampled_rows(B, H, T, seed, n_rand=24):
-    rng = np.random.default_rng(seed)
-    rows = []
-    for b in sorted({0, B - 1}):
-        for h in sorted({0, H // 2 + 1, H - 1}):
-            for i in sorted({0, 1, 63, 64, 127, 128, 255, T // 2, T - 2, T - 1}):
-                rows.append((b, h, i))
-    for _ in range(n_rand):
-        rows.append((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(T))))
-    return rows
-
-
+# --------------------------------------------------- full size, every element
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["llama3", "alibi"])
-def test_full_size_prefill_sampled(name):
+def test_full_size_prefill_every_element(name):
+    """The full Llama-3-8B and ALiBi-MHA prefills (the benchmark's inputs and grid) against
+    the oracle on every output element and every lse (fp32 output); the bf16 output of
+    the same call equals the RNE rounding of the fp32 output bitwise ("Write attention
+    from scratch", Exercise 2: the whole output equals the full computation)."""
     w = W.PREFILL_WORKLOADS[name]
     print(f"[full-size] {w.name}", flush=True)
     q, k, v = W.prefill_inputs(w)
     out, lse = gpu_prefill(q, k, v, pos0=w.pos0, rope_base=w.rope_base, causal=w.causal, alibi=w.alibi)
-    rows = sampled_rows(w.B, w.H, w.T, 31)
+    out16, _ = gpu_prefill(q, k, v, pos0=w.pos0, rope_base=w.rope_base, causal=w.causal, alibi=w.alibi,
+                           out_dtype=torch.bfloat16)
+    assert torch.equal(out16, out.to(torch.bfloat16))
+    got, got_lse = to64(out), to64(lse)
+    del out, out16
     ref, ref_lse = attention_prefill(to64(q), to64(k), to64(v), pos0=w.pos0, rope_base=w.rope_base,
-                                     causal=w.causal, alibi=w.alibi, rows=rows)
-    idx = torch.tensor(rows)
-    got = out[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
-    got_lse = lse[idx[:, 0], idx[:, 1], idx[:, 2]].double().cpu().numpy()
-    assert torch.isfinite(out).all().item()
+                                     causal=w.causal, alibi=w.alibi)
     err = np.abs(got - ref).max()
+    lerr = np.abs(got_lse - ref_lse).max()
+    print(f"  every element: max abs err {err:.3g}, lse {lerr:.3g}", flush=True)
+    assert np.isfinite(got).all()
     assert err <= 1e-2, err
-    assert np.abs(got_lse - ref_lse).max() <= 2e-2
+    assert lerr <= 1e-2, lerr
+
+
+@pytest.mark.parametrize("name", ["llama3", "alibi"])
+def test_full_size_determinism_and_causality_bitwise(name):
+    """On the full-size grids (XCD-mapped workgroup numbering): two calls give the same
+    bits, and perturbing the last token's q, k and v leaves every earlier row bitwise
+    unchanged (the lab's causality property) while the last row moves."""
+    w = W.PREFILL_WORKLOADS[name]
+    q, k, v = W.prefill_inputs(w)
+    kw = dict(pos0=w.pos0, rope_base=w.rope_base, causal=w.causal, alibi=w.alibi, out_dtype=torch.bfloat16)
+    a, la = gpu_prefill(q, k, v, **kw)
+    b, lb = gpu_prefill(q, k, v, **kw)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    for t in (q2, k2, v2):
+        t[:, :, -1] = (t[:, :, -1].float() + 1.0).to(t.dtype)
+    c, lc = gpu_prefill(q2, k2, v2, **kw)
+    assert torch.equal(c[:, :, :-1], a[:, :, :-1]) and torch.equal(lc[:, :, :-1], la[:, :, :-1])
+    assert not torch.equal(c[:, :, -1], a[:, :, -1])
 
 
 # -------------------------------------------------------------------- decode
 def gpu_decode(inp: W.DecodeInputs, rope_base, alibi=0, out_dtype=torch.float32):
+    """The decode step through the binding, with guard bands around out, lse, the
+    workspace and both caches (the step writes one slot of each cache)."""
     lens = torch.from_numpy(inp.lens).cuda()
-    kc, vc = inp.k_cache.cuda(), inp.v_cache.cuda()
+    kc, vc = Guarded.like(inp.k_cache), Guarded.like(inp.v_cache)
     B, H, hd = inp.q.shape
-    out = torch.full((B, H, hd), float("nan"), dtype=out_dtype, device="cuda")
-    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
-    bd.decode(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda(), kc, vc, lens, rope_base=rope_base, alibi=alibi,
-              out=out, lse=lse, out_dtype=out_dtype)
-    torch.cuda.synchronize()
-    return out, lse, kc, vc
+    KV, Lmax = inp.k_cache.shape[1], inp.k_cache.shape[2]
+    out = Guarded((B, H, hd), out_dtype)
+    lse = Guarded((B, H), torch.float32)
+    ws = Guarded((bd.attn_decode_workspace_bytes(B, H, KV, hd, Lmax),), torch.uint8, fill=0)
+    bd.decode(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda(), kc.t, vc.t, lens, rope_base=rope_base, alibi=alibi,
+              out=out.t, lse=lse.t, out_dtype=out_dtype, workspace=ws.t)
+    check_all(out=out, lse=lse, workspace=ws, k_cache=kc, v_cache=vc)
+    return out.t, lse.t, kc.t, vc.t
 
 
 def check_decode_ragged(w, dtype, alibi, lens, lmax):
@@ -357,7 +388,7 @@ def check_decode_ragged(w, dtype, alibi, lens, lmax):
                                             to64(inp.v_cache), lens, rope_base=w.rope_base, alibi=alibi)
     tol = 1e-2 if dtype == "bf16" else 1e-5
     assert np.abs(to64(out) - ref).max() <= tol
-    assert np.abs(to64(lse) - ref_lse).max() <= (2e-2 if dtype == "bf16" else 1e-5)
+    assert np.abs(to64(lse) - ref_lse).max() <= (1e-2 if dtype == "bf16" else 1e-5)
     kc64, vc64 = to64(kc), to64(vc)
     for b, L in enumerate(lens):
         kt = 2.0 ** -8 if dtype == "bf16" else 1e-6   # slot written in the cache dtype
@@ -406,26 +437,29 @@ def test_decode_cache_slab_over_2gib():
     ref, ref_lse, ks, vs = attention_decode(to64(inp.q), to64(inp.k_new), to64(inp.v_new), f32(inp.k_cache),
                                             f32(inp.v_cache), lens, rope_base=w.rope_base, alibi=1)
     assert np.abs(to64(out) - ref).max() <= 1e-2
-    assert np.abs(to64(lse) - ref_lse).max() <= 2e-2
+    assert np.abs(to64(lse) - ref_lse).max() <= 1e-2
     assert np.abs(slot_k - ks[0]).max() <= 2.0 ** -8 * max(1.0, np.abs(ks[0]).max())
     assert np.array_equal(slot_v, vs[0])
 
 
-def test_decode_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_decode_full_size_every_sequence():
+    """The 64-sequence decode workload (lengths 519..8186) on every sequence and head:
+    output and lse against the oracle, and the slot each sequence appended."""
     w = W.KV_DECODE
     print(f"[full-size decode] {w.name}", flush=True)
     inp = W.decode_inputs(w)
     out, lse, kc, vc = gpu_decode(inp, w.rope_base)
     assert torch.isfinite(out).all().item()
     lens = inp.lens
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63})
-    kcs = to64(inp.k_cache[pick])
-    vcs = to64(inp.v_cache[pick])
-    ref, ref_lse, _, _ = attention_decode(to64(inp.q[pick]), to64(inp.k_new[pick]), to64(inp.v_new[pick]),
-                                          kcs, vcs, lens[pick], rope_base=w.rope_base)
-    got = to64(out[pick])
-    assert np.abs(got - ref).max() <= 1e-2
-    assert np.abs(to64(lse[pick]) - ref_lse).max() <= 2e-2
+    ref, ref_lse, ks, vs = attention_decode(to64(inp.q), to64(inp.k_new), to64(inp.v_new), to64(inp.k_cache),
+                                            to64(inp.v_cache), lens, rope_base=w.rope_base)
+    err, lerr = np.abs(to64(out) - ref).max(), np.abs(to64(lse) - ref_lse).max()
+    print(f"  every sequence: max abs err {err:.3g}, lse {lerr:.3g}", flush=True)
+    assert err <= 1e-2 and lerr <= 1e-2
+    for b, L in enumerate(lens):
+        assert np.abs(to64(kc[b, :, L]) - ks[b]).max() <= 2.0 ** -8 * max(1.0, np.abs(ks[b]).max())
+        assert np.array_equal(to64(vc[b, :, L]), vs[b])
 
 
 def test_decode_long_split_path():
@@ -445,7 +479,7 @@ def test_decode_long_split_path():
                                             to64(inp.k_cache[pick]), to64(inp.v_cache[pick]), lens[pick],
                                             rope_base=w.rope_base, alibi=1)
     assert np.abs(to64(out[pick]) - ref).max() <= 1e-2
-    assert np.abs(to64(lse[pick]) - ref_lse).max() <= 2e-2
+    assert np.abs(to64(lse[pick]) - ref_lse).max() <= 1e-2
     for i, b in enumerate(pick):
         L = int(lens[b])
         assert np.array_equal(to64(vc[b, :, L]), vs[i])
@@ -454,14 +488,16 @@ def test_decode_long_split_path():
 # ------------------------------------------------------------- fp8 decode
 def gpu_decode_fp8(inp: W.DecodeInputs, w: W.DecodeWorkload, alibi=0, out_dtype=torch.float32):
     lens = torch.from_numpy(inp.lens).cuda()
-    kc, vc = inp.k_cache.cuda(), inp.v_cache.cuda()
+    kc, vc = Guarded.like(inp.k_cache), Guarded.like(inp.v_cache)
     B, H, hd = inp.q.shape
-    out = torch.full((B, H, hd), float("nan"), dtype=out_dtype, device="cuda")
-    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
-    bd.decode_fp8(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda(), kc, vc, lens, w.k_scale, w.v_scale,
-                  rope_base=w.rope_base, alibi=alibi, out=out, lse=lse, out_dtype=out_dtype)
-    torch.cuda.synchronize()
-    return out, lse, kc.cpu(), vc.cpu()
+    KV, Lmax = inp.k_cache.shape[1], inp.k_cache.shape[2]
+    out = Guarded((B, H, hd), out_dtype)
+    lse = Guarded((B, H), torch.float32)
+    ws = Guarded((bd.attn_decode_workspace_bytes(B, H, KV, hd, Lmax),), torch.uint8, fill=0)
+    bd.decode_fp8(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda(), kc.t, vc.t, lens, w.k_scale, w.v_scale,
+                  rope_base=w.rope_base, alibi=alibi, out=out.t, lse=lse.t, out_dtype=out_dtype, workspace=ws.t)
+    check_all(out=out, lse=lse, workspace=ws, k_cache=kc, v_cache=vc)
+    return out.t, lse.t, kc.t.cpu(), vc.t.cpu()
 
 
 def check_slot_codes(got, ref, pre):
@@ -545,14 +581,16 @@ def test_decode_fp8_matches_bf16_decode_of_the_dequantized_cache():
 # ---------------------------------------------------------- latent decode
 def gpu_decode_latent(inp: W.LatentInputs, alibi=0, out_dtype=torch.float32):
     lens = torch.from_numpy(inp.lens).cuda()
-    cc = inp.c_cache.cuda()
+    cc = Guarded.like(inp.c_cache)
     B, H, hd = inp.q.shape
-    out = torch.full((B, H, hd), float("nan"), dtype=out_dtype, device="cuda")
-    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
-    bd.decode_latent(inp.q.cuda(), inp.c_new.cuda(), cc, lens, inp.w_uk.cuda(), inp.w_uv.cuda(), alibi=alibi,
-                     out=out, lse=lse, out_dtype=out_dtype)
-    torch.cuda.synchronize()
-    return out, lse, cc.cpu()
+    Lmax, dc = inp.c_cache.shape[1], inp.c_cache.shape[2]
+    out = Guarded((B, H, hd), out_dtype)
+    lse = Guarded((B, H), torch.float32)
+    ws = Guarded((bd.attn_decode_latent_workspace_bytes(B, H, dc, Lmax),), torch.uint8, fill=0)
+    bd.decode_latent(inp.q.cuda(), inp.c_new.cuda(), cc.t, lens, inp.w_uk.cuda(), inp.w_uv.cuda(), alibi=alibi,
+                     out=out.t, lse=lse.t, out_dtype=out_dtype, workspace=ws.t)
+    check_all(out=out, lse=lse, workspace=ws, c_cache=cc)
+    return out.t, lse.t, cc.t.cpu()
 
 
 @pytest.mark.parametrize("H,hd,dc", [(16, 128, 512), (12, 64, 256), (40, 128, 256), (4, 64, 512)])

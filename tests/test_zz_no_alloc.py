@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from guards import Guarded, check_all
 from transformer_attention_02_amd import binding as bd
 from transformer_attention_02_amd import workloads as W
 
@@ -22,15 +23,15 @@ def run_pair(B, H, KV, hd, lens, lmax, dtype, alibi, seed, out_dtype=torch.float
     kc_ref, vc_ref = inp.k_cache.cuda(), inp.v_cache.cuda()
     kc, vc = kc_ref.clone(), vc_ref.clone()
     out_ref, lse_ref = bd.decode(q, kn, vn, kc_ref, vc_ref, lens_d, alibi=alibi, out_dtype=out_dtype)
-    out = torch.full_like(out_ref, float("nan"))
-    lse = torch.full_like(lse_ref, float("nan"))
+    gout, glse = Guarded(out_ref.shape, out_ref.dtype), Guarded(lse_ref.shape, torch.float32)
+    out, lse = gout.t, glse.t
     dt = bd.ATTN_DTYPE_BF16 if q.dtype == torch.bfloat16 else bd.ATTN_DTYPE_F32
     odt = bd.ATTN_DTYPE_BF16 if out.dtype == torch.bfloat16 else bd.ATTN_DTYPE_F32
     st = bd.attn_decode_fwd_noalloc(q.data_ptr(), kn.data_ptr(), vn.data_ptr(), kc.data_ptr(), vc.data_ptr(),
                                     lens_d.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, KV, hd, lmax,
                                     10000.0, alibi, dt, odt, torch.cuda.current_stream().cuda_stream)
     assert st == bd.ATTN_OK, bd.attn_last_error()
-    torch.cuda.synchronize()
+    check_all(out=gout, lse=glse)
     assert torch.isfinite(out).all().item()
     assert torch.equal(out, out_ref) and torch.equal(lse, lse_ref)
     assert torch.equal(kc, kc_ref) and torch.equal(vc, vc_ref)

@@ -15,7 +15,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libattn.so")
+# ATTN_LIB selects another build of the same library (the sanitizer build of
+# the checks); there is no fallback either way.
+LIB_PATH = os.environ.get("ATTN_LIB") or os.path.join(PKG, "libattn.so")
 
 ATTN_OK = 0
 ATTN_ERR_NULL = 1

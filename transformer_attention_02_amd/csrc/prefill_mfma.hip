@@ -32,7 +32,8 @@
 //     bf16); K arrives already rotated (a pre-pass writes it once).
 //   * Workgroups are numbered so that every workgroup touching one key/value
 //     head lands on the same XCD (its L2 keeps that head's K/V), heaviest
-//     causal blocks first.
+//     causal blocks first; an XCD works through its heads a few at a time, as
+//     many as keep their K/V within its 4 MiB L2.
 #include <type_traits>
 
 #include "mfma_tile.h"
@@ -55,6 +56,7 @@ struct GridMap {
   int nqb;       // query blocks
   int units;     // B * KV * hchunks
   int xcd_aware;
+  int ugroup;    // units an XCD works on at a time
 };
 
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
@@ -171,10 +173,15 @@ struct WaveState {
       }
     }
     if constexpr (MASK) {
+      // register i holds key k0 + 8hf + c_i (c_i a constant): it is visible when
+      // lo <= c_i <= hi, the per-lane limits folding the causal bound (key <= qi),
+      // the sequence end (key < Tk) and the window start (key > qi - window)
+      const int hi = min(CAUSAL ? -dbase : 0x7fffffff, Tk - 1 - k0 - 8 * hf);
+      const int lo = WINDOW ? 1 - window - dbase : 0;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const int dk = dbase + 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
-        const bool vis = (dk + qi < Tk) && (!CAUSAL || dk <= 0) && (!WINDOW || dk > -window);
+        const int ci = 32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8);
+        const bool vis = WINDOW ? (ci <= hi && ci >= lo) : ci <= hi;
         t[i] = vis ? t[i] : -INFINITY;
       }
     }
@@ -262,13 +269,17 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   int unit, qrank;
   if (gm.xcd_aware) {
     // Consecutive workgroups go round-robin to the 8 XCDs. XCD x owns units
-    // [x*upx, (x+1)*upx) and interleaves them, heaviest query blocks first.
-    // (Working through one unit at a time measured slower: all of an XCD's
-    // workgroups then hit the same K/V lines at once.)
+    // [x*upx, (x+1)*upx) and works through them in groups of gm.ugroup units
+    // whose K/V fit its L2, interleaving a group's units, heaviest query
+    // blocks first. (Working through one unit at a time measured slower: all
+    // of an XCD's workgroups then hit the same K/V lines at once.)
     const int upx = gm.units >> 3;
     const int j = w >> 3;
-    unit = (w & 7) * upx + j % upx;
-    qrank = j / upx;
+    const int per_group = gm.ugroup * gm.nqb;
+    const int g = j / per_group, r = j % per_group;
+    const int gsz = min(gm.ugroup, upx - g * gm.ugroup);
+    unit = (w & 7) * upx + g * gm.ugroup + r % gsz;
+    qrank = r / gsz;
   } else {
     unit = w % gm.units;
     qrank = w / gm.units;
@@ -442,6 +453,17 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   if constexpr (WINDOW) {
     if (kt + 3 <= kc_hi) pending = true;  // every active wave runs a clean tile
   }
+  // Clean tiles six per iteration (two turns of the ring): with an even step
+  // count the pending probabilities can alternate between two register sets
+  // instead of being copied at every step; then three at a time.
+  for (; kt + 6 <= kc_hi; kt += 6) {
+    step(kt, F{}, P0{});
+    step(kt + 1, F{}, P1{});
+    step(kt + 2, F{}, P2{});
+    step(kt + 3, F{}, P0{});
+    step(kt + 4, F{}, P1{});
+    step(kt + 5, F{}, P2{});
+  }
   for (; kt + 3 <= kc_hi; kt += 3) {
     step(kt, F{}, P0{});
     step(kt + 1, F{}, P1{});
@@ -486,6 +508,13 @@ GridMap make_grid(const PrefillArgs& a) {
   gm.nqb = (a.Tq + gm.bm - 1) / gm.bm;
   gm.units = a.B * a.KV * gm.hchunks;
   gm.xcd_aware = (gm.units % 8) == 0;
+  // units per XCD group: their K/V (2 * Tk * hd * 2 bytes each) within 4 MiB,
+  // the L2 of one XCD, but at least 32 workgroups (one per CU of the XCD)
+  const long unit_bytes = 4L * a.Tk * a.hd;
+  const int upx = gm.units >> 3;
+  int ug = (int)max(1L, (4L << 20) / unit_bytes);
+  while (ug * gm.nqb < 32 && ug < upx) ++ug;
+  gm.ugroup = max(1, min(ug, upx));
   return gm;
 }
 
