@@ -121,7 +121,7 @@ def traffic_for(kernel, sources, workload):
             tab = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = tab.get(kernel)
+    ent = tab.get(f"{kernel} @ {workload}")
     if not ent or ent.get("source_digest") != source_digest(sources) or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
@@ -367,6 +367,87 @@ class Backward:
         return self.w.bwd_flops()
 
 
+def host_info():
+    """Host CPU count and model (from /proc/cpuinfo) for the CPU-baseline records."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cpus": os.cpu_count(), "cpu_model": model}
+
+
+def measure_ceilings(torch, dev, mfma, hbm):
+    """Same-run context for the rooflines, measured before the timed steps (the
+    heavy work also brings the clock to its steady state first).
+
+    mfma: the vendor GEMM (torch.matmul -> hipBLASLt) on N(0,1) bf16 operands.
+    The published 2.5 PFLOP/s assumes the 2.4 GHz peak clock; with random data
+    the chip runs power-limited well below it.
+    hbm: a read-only stream of 4 GiB (libattn_probe.so: non-temporal 16-byte
+    loads, every byte read once) and a torch copy of 2 GiB.
+    """
+    res = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    if mfma:
+        n = 8192
+        g = torch.Generator(device=dev).manual_seed(11)
+        a_ = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+        b_ = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+        for _ in range(10):
+            c_ = a_ @ b_
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            c_ = a_ @ b_
+        e1.record()
+        torch.cuda.synchronize()
+        res["gemm_bf16_tflops"] = 2.0 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+        res["gemm"] = f"torch.matmul {n}x{n}x{n} bf16, N(0,1) operands"
+        del a_, b_, c_
+    if hbm:
+        probe = ctypes.CDLL(os.path.join(ROOT, "transformer_attention_02_amd", "libattn_probe.so"))
+        probe.attn_probe_read_stream.restype = ctypes.c_int
+        probe.attn_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        probe.attn_probe_sink_words.restype = ctypes.c_size_t
+        x_ = torch.ones(1 << 31, dtype=torch.bfloat16, device=dev)
+        sink = torch.empty(probe.attn_probe_sink_words(), dtype=torch.int32, device=dev)
+        nb = x_.numel() * x_.element_size()
+        stream = torch.cuda.current_stream().cuda_stream
+        run = lambda: probe.attn_probe_read_stream(x_.data_ptr(), nb, sink.data_ptr(), stream)  # noqa: E731
+        for _ in range(5):
+            assert run() == 0
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        res["hbm_read_stream_gbs"] = nb / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+        res["hbm_read_stream"] = "read-only stream of 4 GiB, non-temporal 16-byte loads (libattn_probe.so)"
+        y_ = torch.empty(1 << 30, dtype=torch.bfloat16, device=dev)
+        src = x_[: y_.numel()]
+        for _ in range(3):
+            y_.copy_(src)
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            y_.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        res["hbm_copy_gbs"] = 2 * y_.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+        res["hbm_copy"] = "torch copy of 2 GiB (read + write bytes)"
+        del x_, y_, sink
+    return res
+
+
 def cpu_baseline_leg(pre, dec, heads, seqs):
     """The fp64 oracle on a bounded sample of the same workload (rank 0, N=1 only)."""
     import numpy as np
@@ -376,7 +457,7 @@ def cpu_baseline_leg(pre, dec, heads, seqs):
     from oracle import attention_decode, attention_prefill
 
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    res = {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count()}
+    res = {"kind": "oracle", "cores": threads, **host_info()}
     f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
     if pre is not None:
         w = pre.w
@@ -440,7 +521,7 @@ def cpu_baseline_fp8(dec8, seqs):
         t_total += time.perf_counter() - t0
         nbytes += (L + 1) * w.KV * w.hd * 2
         errs.append(float(np.abs(f64(dec8.out[b:b + 1]) - ref).max()))
-    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": nbytes / t_total / 1e9,
+    return {"kind": "oracle", "cores": threads, **host_info(), "value": nbytes / t_total / 1e9,
             "unit": "GB/s", "seconds": t_total, "sample": f"sequences 0..{len(pick) - 1} of {w.B}",
             "max_abs_err_vs_gpu_bf16_out": max(errs)}
 
@@ -467,7 +548,7 @@ def cpu_baseline_latent(lat, seqs):
         t_total += time.perf_counter() - t0
         nbytes += (L + 1) * w.dc * 2
         errs.append(float(np.abs(f64(lat.out[b:b + 1]) - ref).max()))
-    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": nbytes / t_total / 1e9,
+    return {"kind": "oracle", "cores": threads, **host_info(), "value": nbytes / t_total / 1e9,
             "unit": "GB/s", "seconds": t_total, "sample": f"sequences 0..{len(pick) - 1} of {w.B}",
             "max_abs_err_vs_gpu_bf16_out": max(errs)}
 
@@ -495,7 +576,7 @@ def cpu_baseline_proj(pj, seqs):
         err = max(err, float(np.abs(f64(pj.q[b:b + 1]) - q).max()), float(np.abs(f64(pj.k[b:b + 1]) - k).max()),
                   float(np.abs(f64(pj.v[b:b + 1]) - v).max()), float(np.abs(f64(pj.y[b:b + 1]) - y).max()))
     flops = n * w.T * (2.0 * w.N_qkv * w.D + 2.0 * w.D * w.H * w.hd)
-    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": flops / secs / 1e12,
+    return {"kind": "oracle", "cores": threads, **host_info(), "value": flops / secs / 1e12,
             "unit": "TFLOP/s", "seconds": secs, "sample": f"sequences 0..{n - 1} of {w.B} (both projections)",
             "max_abs_err_vs_gpu_bf16": err}
 
@@ -521,7 +602,7 @@ def cpu_baseline_block(blk, tokens):
     secs = time.perf_counter() - t0
     flops = 2.0 * T * pw.N_qkv * pw.D + 4.0 * pw.H * pw.hd * T * (T + 1) / 2 + 2.0 * T * pw.D * pw.H * pw.hd
     err = float(np.abs(f64(blk.y[:1, :T]) - y).max())
-    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": flops / secs / 1e12,
+    return {"kind": "oracle", "cores": threads, **host_info(), "value": flops / secs / 1e12,
             "unit": "TFLOP/s", "seconds": secs, "sample": f"the block on tokens 0..{T - 1} of sequence 0",
             "max_abs_err_vs_gpu_bf16": err}
 
@@ -546,7 +627,7 @@ def cpu_baseline_bwd(bwd, heads):
     dt = time.perf_counter() - t0
     flops = 10.0 * heads * w.hd * w.pairs()
     err = float(np.abs(f64(bwd.dq[0:1, :heads]) - dq).max())
-    return {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "value": flops / dt / 1e12,
+    return {"kind": "oracle", "cores": threads, **host_info(), "value": flops / dt / 1e12,
             "unit": "TFLOP/s", "seconds": dt,
             "sample": f"{heads} query heads of batch 0 ({heads // g} KV heads), all {w.T} rows: "
                       f"{flops / w.bwd_flops() * 100:.2f}% of the backward step",
@@ -564,7 +645,8 @@ def main():
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the same-run library GEMM that gives the practical bf16 matrix-core ceiling")
+                    help="skip the same-run ceilings measured before the timed steps: the library GEMM (practical "
+                         "bf16 matrix-core ceiling) and the read-only HBM stream")
     ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--cpu-heads-bwd", type=int, default=16)
@@ -620,6 +702,10 @@ def main():
     bwd = Backward(W.LLAMA3_8B, dev, bd, W, torch, stream) if args.workload == "backward" else None
     log(f"inputs ready: prefill={pre_w.name if pre else None} decode={dec.w.name if dec else None} "
         f"backward={bwd.w.name if bwd else None}")
+    ceilings = None
+    if not args.no_ceilings and (pre or bwd or dec or dec8 or lat):
+        ceilings = measure_ceilings(torch, dev, mfma=bool(pre or bwd), hbm=bool(dec or dec8 or lat))
+        log(f"same-run ceilings: {ceilings}")
 
     for _ in range(args.warmup):
         if pre:
@@ -702,9 +788,11 @@ def main():
             cfg["prefill"].update(query_rows=w.rows, q_offset=w.q_offset, window=w.window)
         cfg["prefill"]["kernel_ms_median"], cfg["prefill"]["kernel_ms_min"] = med_min("pk")
         traffic = traffic_for("prefill_mfma_kernel", PREFILL_SOURCES, w.name)
+        # frac is the attention kernel's; frac_call counts the whole call, the K
+        # rotation pre-pass included
         line["roofline"] = {"bound": "mfma", "achieved": kt, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": kt / PEAK_BF16_TFLOPS, "traffic": traffic,
-                            "kernel": f"prefill_mfma_kernel<{w.hd}>"}
+                            "kernel": f"prefill_mfma_kernel<{w.hd}>", "frac_call": tflops / PEAK_BF16_TFLOPS}
     if dec:
         w = dec.w
         dc, dk = avg("dc"), avg("dk")
@@ -836,28 +924,15 @@ def main():
     line["outputs_finite"] = ok
     hip.close()
 
-    if (pre or bwd) and not args.no_ceilings:
-        # Same-run context for the matrix-core roofline: the vendor GEMM (torch.matmul ->
-        # hipBLASLt) on N(0,1) bf16 operands. The published 2.5 PFLOP/s assumes the 2.4 GHz
-        # peak clock; with random data the chip runs power-limited well below it.
-        n = 8192
-        g = torch.Generator(device=dev).manual_seed(11)
-        a_ = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
-        b_ = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
-        for _ in range(3):
-            c_ = a_ @ b_
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(10):
-            c_ = a_ @ b_
-        e1.record()
-        torch.cuda.synchronize()
-        gemm = 2.0 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
-        line["measured_ceilings"] = {"gemm_bf16_tflops": gemm,
-                                     "gemm": f"torch.matmul {n}x{n}x{n} bf16, N(0,1) operands",
-                                     "prefill_kernel_vs_gemm": line["roofline"]["achieved"] / gemm}
-        del a_, b_, c_
+    if ceilings is not None:
+        mc = dict(ceilings)
+        if (pre or bwd) and "gemm_bf16_tflops" in mc:
+            mc["prefill_kernel_vs_gemm" if pre else "kernel_vs_gemm"] = line["roofline"]["achieved"] / mc["gemm_bf16_tflops"]
+        dk = line.get("decode", {}).get("roofline", {}).get("achieved") if pre else (
+            line["roofline"]["achieved"] if (dec or dec8 or lat) else None)
+        if dk and "hbm_read_stream_gbs" in mc:
+            mc["decode_kernel_vs_read_stream"] = dk / mc["hbm_read_stream_gbs"]
+        line["measured_ceilings"] = mc
 
     if not args.no_cpu_baseline and blk:
         log("cpu baseline: timing the fp64 oracle block on a bounded sample ...")
