@@ -478,25 +478,66 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   }
 
   const float l_tot = ws.l_run + xhalf(ws.l_run);
-  const int qi = qw0 + n;  // query row
-  if (qi >= a.Tq) return;
   const float inv_l = 1.0f / l_tot;
-  const long orow = (((long)b * a.H + head) * a.Tq + qi) * HD;
+  if constexpr (OUT_BF16) {
+    // bf16 O leaves through LDS so that every store instruction writes whole
+    // rows: the wave puts its 32 rows, in the accumulator layout, into a
+    // private slot (a quarter of one of the two ring stages the last tile does
+    // not occupy; no wave reads those any more and no DMA is in flight), then
+    // reads them back row-major. 16-byte chunks are XOR-swizzled by row, so
+    // neither side has bank conflicts.
+    constexpr int RB = 2 * HD;    // bytes of one output row
+    constexpr int CPR = RB / 16;  // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR; // rows per read-back instruction
+    // (lane indices re-derived here, so the compiler does not compute the
+    // epilogue's addresses before the loop and hold them through it)
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int en = el & 31, ehf = el >> 5;
+    const int p_last = (nkt - 1 - kt_begin) % 3;
+    unsigned char* fs = (wave < 4) ? (p_last == 0 ? s1 : s0) : (p_last == 2 ? s1 : s2);
+    LDS unsigned char* slot = (LDS unsigned char*)(fs + (wave & 3) * (C::STAGE / 4));
 #pragma unroll
-  for (int mb = 0; mb < HD / 32; ++mb) {
+    for (int mb = 0; mb < HD / 32; ++mb) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * mb + 8 * g4 + 4 * hf;
-      const float o0 = ws.oacc[mb][4 * g4 + 0] * inv_l, o1 = ws.oacc[mb][4 * g4 + 1] * inv_l;
-      const float o2 = ws.oacc[mb][4 * g4 + 2] * inv_l, o3 = ws.oacc[mb][4 * g4 + 3] * inv_l;
-      if constexpr (OUT_BF16) {
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d) =
-            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-      } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + d) = make_float4(o0, o1, o2, o3);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = 4 * mb + g4;  // chunk of d = 32mb + 8g4 .. +7; this lane holds half 'ehf' of it
+        LDS unsigned char* dst = slot + en * RB + ((c ^ (en % CPR)) * 16) + 8 * ehf;
+        const float o0 = ws.oacc[mb][4 * g4 + 0] * inv_l, o1 = ws.oacc[mb][4 * g4 + 1] * inv_l;
+        const float o2 = ws.oacc[mb][4 * g4 + 2] * inv_l, o3 = ws.oacc[mb][4 * g4 + 3] * inv_l;
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<LDS u32x2*>(dst) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const long obase = ((long)b * a.H + head) * a.Tq + qw0;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + el / CPR, c = el % CPR;
+      const u32x4 v = *reinterpret_cast<const LDS u32x4*>(slot + r * RB + ((c ^ (r % CPR)) * 16));
+      if (qw0 + r < a.Tq)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + (obase + r) * HD + c * 8) = v;
+    }
+  } else {
+    const int qi = qw0 + n;
+    if (qi < a.Tq) {
+      const long orow = (((long)b * a.H + head) * a.Tq + qi) * HD;
+#pragma unroll
+      for (int mb = 0; mb < HD / 32; ++mb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * mb + 8 * g4 + 4 * hf;
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + d) =
+              make_float4(ws.oacc[mb][4 * g4 + 0] * inv_l, ws.oacc[mb][4 * g4 + 1] * inv_l,
+                          ws.oacc[mb][4 * g4 + 2] * inv_l, ws.oacc[mb][4 * g4 + 3] * inv_l);
+        }
       }
     }
   }
+  const int qi = qw0 + n;  // query row
+  if (qi >= a.Tq) return;
   if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.Tq + qi] = (ws.m_run + log2f(l_tot)) * 0.69314718055994531f;
 }
 
