@@ -306,10 +306,16 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   const int nkt = CAUSAL ? (tq_last / BN + 1) : (a.Tk + BN - 1) / BN;
   const int kt_begin = WINDOW ? max(0, tq0 - a.window + 1) / BN : 0;
 
+  // Causal ALiBi walks the key tiles from the last one down: each row meets
+  // its largest bias (the keys nearest its token) first, so its running max
+  // is set at once instead of rising tile by tile (which forced a rescale of
+  // O on most steps). Other variants walk upwards; the online softmax gives
+  // the same result in any order, up to rounding.
+  constexpr bool REV = ALIBI && CAUSAL && !WINDOW;
   // The first K/V tile streams into stage 0 during the Q set-up.
   Dma<HD, NW> dma;
   dma.init(wave, lane);
-  dma.issue(Kg, Vg, kt_begin, a.Tk, s0, wave);
+  dma.issue(Kg, Vg, REV ? nkt - 1 : kt_begin, a.Tk, s0, wave);
   // Stage 2 stands in for the tile before the first one: its V part is zeroed
   // and the pending probabilities start at zero, so the first tile's deferred
   // product adds exact zeros.
@@ -394,7 +400,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // pprev owes its V^T product. Without a window every active wave runs the
   // first tile, so this starts true (the zero operands of "tile -1" are
   // harmless); with a window a wave may skip the first tiles and starts false.
-  bool pending = !WINDOW;
+  bool pending = !WINDOW && !REV;
   auto step = [&](int kt, auto mask_tag, auto phase_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(phase_tag)::value;
@@ -402,7 +408,11 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     unsigned char* prv = P == 0 ? s2 : (P == 1 ? s0 : s1);
     unsigned char* nxt = P == 0 ? s1 : (P == 1 ? s2 : s0);
     const int k0 = kt * BN;
-    if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.Tk, nxt, wave);
+    if constexpr (REV) {
+      if (kt > kt_begin) dma.issue(Kg, Vg, kt - 1, a.Tk, nxt, wave);
+    } else {
+      if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.Tk, nxt, wave);
+    }
     // in a masked tile a wave may be past its last visible key (causal) or
     // before its first one (sliding window)
     const int tw0 = a.q_off + qw0;
@@ -416,7 +426,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       __builtin_amdgcn_s_setprio(1);
       ws.template softmax_pv<MASK>(sa, sb, k0, (LdsBytes)(prv + C::K_BYTES));
       __builtin_amdgcn_s_setprio(0);
-      if constexpr (MASK && WINDOW) pending = true;
+      if constexpr (MASK && (WINDOW || REV)) pending = true;
     } else if (MASK && pending) {
       // past the wave's last visible key: settle the owed product (the wave
       // does not run again)
@@ -445,6 +455,44 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       ++kt;
     }
   };
+  if constexpr (REV) {
+    // Step i takes tile nkt-1-i into ring stage i % 3. The masked tiles at the
+    // top come first, in whole rounds of the ring (a round that is not all
+    // masked runs masked), then the clean tiles. A wave skips the masked tiles
+    // past its last token and runs every tile from its first visible one on.
+    const int total = nkt - kt_begin;
+    const int mend = min(total, (nkt - kc_hi + 2) / 3 * 3);
+    int i = 0;
+    auto masked_rev = [&](int end) __attribute__((always_inline)) {
+      while (i < end) {
+        step(nkt - 1 - i, M{}, P0{});
+        if (++i >= end) break;
+        step(nkt - 1 - i, M{}, P1{});
+        if (++i >= end) break;
+        step(nkt - 1 - i, M{}, P2{});
+        ++i;
+      }
+    };
+    masked_rev(mend);
+    for (; i + 6 <= total; i += 6) {
+      step(nkt - 1 - i, F{}, P0{});
+      step(nkt - 2 - i, F{}, P1{});
+      step(nkt - 3 - i, F{}, P2{});
+      step(nkt - 4 - i, F{}, P0{});
+      step(nkt - 5 - i, F{}, P1{});
+      step(nkt - 6 - i, F{}, P2{});
+    }
+    for (; i + 3 <= total; i += 3) {
+      step(nkt - 1 - i, F{}, P0{});
+      step(nkt - 2 - i, F{}, P1{});
+      step(nkt - 3 - i, F{}, P2{});
+    }
+    // the last one or two clean tiles (the ring is at stage 0 here)
+    if (i < total) step(nkt - 1 - i, F{}, P0{});
+    if (i + 1 < total) step(nkt - 2 - i, F{}, P1{});
+    // the last step took tile kt_begin = 0, which every row sees
+    pending = true;
+  } else {
   if constexpr (WINDOW) {
     // tiles at the window's start, up to the first round boundary at or after
     // the first clean tile
@@ -470,6 +518,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     step(kt + 2, F{}, P2{});
   }
   masked_rounds(nkt);
+  }
   if (!wave_active) return;
   // the last tile's V^T product (no DMA is in flight any more)
   if (pending) {
