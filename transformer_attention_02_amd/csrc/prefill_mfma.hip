@@ -72,6 +72,11 @@ struct WaveState {
   float l_run;           // this half-wave's part of the running denominator
   float c2;              // log2(e) / sqrt(hd)
   float slope2;          // ALiBi slope * log2(e)
+  // causal ALiBi without a window takes the key-offset part of its bias from
+  // the matrix core (see init_alibi_mfma)
+  static constexpr bool MB = ALIBI && CAUSAL && !WINDOW;
+  bf16x8 kbias[2];       // MB: A operand of the bias k-step for the two 32-key halves
+  bf16x8 qbias;          // MB: its B operand (slope2 / c2 as three bf16 parts)
   int qi;                // this lane's query token (index in the key sequence)
   int Tk;                // keys in the sequence
   int window;            // sliding window in tokens (0: none)
@@ -113,6 +118,11 @@ struct WaveState {
       const bf16x8 av = *reinterpret_cast<const LDS bf16x8*>(kb + k_off<HD>(32 + krow, 2 * s + hf));
       sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[s], sb, 0, 0, 0);
     }
+    if constexpr (MB) {
+      // the key-offset part of the causal ALiBi bias, on the matrix core
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias[0], qbias, sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbias[1], qbias, sb, 0, 0, 0);
+    }
     // Issue order: kKAhead operand reads go out before the first MFMA, then
     // one read per MFMA, so LDS latency hides behind kKAhead MFMAs.
     constexpr int NR = 2 * (HD / 16);
@@ -122,7 +132,30 @@ struct WaveState {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kKAhead + (MB ? 2 : 0), 0);
+  }
+
+  // Causal ALiBi's bias is slope2 * (key - query). The part that varies inside
+  // a tile, slope2 * (key - k0), comes from one more k-step of the S^T MFMAs:
+  // the A-operand row of this lane is key 32 * blk + perm_row(lane % 32) of the
+  // tile, and the first half-wave's k-values 0..2 hold that offset c (exact in
+  // bf16) against B = slope2 / c2 = slope * sqrt(hd) split into three bf16
+  // parts (each the bf16 of what the previous ones leave), so the products are
+  // exact and their fp32 sum gives c * slope * sqrt(hd) to ~2^-24 relative.
+  // The rest, slope2 * (k0 - qi), is one value per lane, added once.
+  __device__ __forceinline__ void init_alibi_mfma() {
+    const int n = lane & 31, hf = lane >> 5;
+    const float sl = slope2 / c2;
+    const __bf16 b0 = (__bf16)sl;
+    const __bf16 b1 = (__bf16)(sl - (float)b0);
+    const __bf16 b2 = (__bf16)(sl - (float)b0 - (float)b1);
+    const __bf16 z = (__bf16)0.0f;
+    qbias = hf == 0 ? bf16x8{b0, b1, b2, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const __bf16 c = (__bf16)(float)(32 * blk + perm_row(n));
+      kbias[blk] = hf == 0 ? bf16x8{c, c, c, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
+    }
   }
 
   // O^T += V^T P^T over four 16-key steps of the V tile at vb. V^T is read
@@ -151,20 +184,24 @@ struct WaveState {
   template <bool MASK>
   __device__ __forceinline__ void softmax_pv(const f32x16& sa, const f32x16& sb, int k0, LdsBytes vprev) {
     const int hf = lane >> 5;
-    // Without ALiBi t keeps the raw scores (the max commutes with the positive
-    // scale, which is folded into the exponent's FMA); with ALiBi t is the
-    // scaled, biased score in log2 units.
+    // t keeps the raw scores (the max commutes with the positive scale, which
+    // is folded into the exponent's FMA), except for ALiBi with a window or
+    // without causality, where t is the scaled, biased score in log2 units.
     float t[32];
     const int dbase = k0 + 8 * hf - qi;  // key - query at register offset 0
-    // ALiBi: register i sits at key - query = dbase + c_i with a constant c_i, so
-    // the bias costs one FMA per score when causal (slope2 * dbase is formed once;
-    // distances are exact in fp32) and an add plus a multiply otherwise.
+    // Register i sits at key - query = dbase + c_i with a constant c_i
+    // (distances are exact in fp32): with a window the causal bias costs one
+    // FMA per score, without causality an add plus a multiply.
     const float dbf = (float)dbase;
-    const float sbase = slope2 * dbf;
+    // MB: the scores arrive with slope2 / c2 * (key - k0) added; what is left
+    // of the bias, slope2 * (k0 - qi), is common to the lane's row. Otherwise
+    // ALiBi is applied here and t holds scaled scores in log2 units.
+    const float sbase = slope2 * (float)(MB ? k0 - qi : dbase);
+    constexpr bool SCALED = ALIBI && !MB;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const float x = i < 16 ? sa[i] : sb[i - 16];
-      if constexpr (ALIBI) {
+      if constexpr (SCALED) {
         const float ci = (float)(32 * (i / 16) + 16 * ((i % 16) / 8) + (i % 8));
         const float bias = CAUSAL ? fmaf(slope2, ci, sbase) : -slope2 * fabsf(dbf + ci);
         t[i] = fmaf(x, c2, bias);
@@ -189,7 +226,8 @@ struct WaveState {
 #pragma unroll
     for (int i = 1; i < 32; ++i) mx = fmaxf(mx, t[i]);
     mx = fmaxf(mx, xhalf(mx));
-    const float ms = ALIBI ? mx : mx * c2;  // tile max in log2 units
+    // tile max in log2 units
+    const float ms = SCALED ? mx : (MB ? fmaf(mx, c2, sbase) : mx * c2);
     // Lazy rescale: a row's running max only moves when its tile max exceeds
     // it by more than 8 (a factor 2^8); otherwise the stale max is kept for
     // both the numerator and the denominator, which leaves O / l unchanged.
@@ -203,9 +241,10 @@ struct WaveState {
     // out as exact zeros, not as exp2(-inf - (-inf)).
     const float mref = (MASK && m_run == -INFINITY) ? 0.f : m_run;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    const float woff = MB ? sbase - mref : -mref;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      t[i] = __builtin_amdgcn_exp2f(ALIBI ? t[i] - mref : fmaf(t[i], c2, -mref));
+      t[i] = __builtin_amdgcn_exp2f(SCALED ? t[i] - mref : fmaf(t[i], c2, woff));
       ls[i % 4] += t[i];
     }
     l_run = fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
@@ -329,6 +368,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   ws.init_offsets();
   ws.c2 = a.scale_log2;
   ws.slope2 = ALIBI ? alibi_slope(a.alibi, head, a.H) * 1.4426950408889634f : 0.f;
+  if constexpr (ALIBI && CAUSAL && !WINDOW) ws.init_alibi_mfma();
   ws.m_run = -INFINITY;
   ws.l_run = 0.f;
 #pragma unroll
