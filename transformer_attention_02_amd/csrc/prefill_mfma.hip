@@ -68,6 +68,7 @@ struct WaveState {
   f32x16 oacc[HD / 32];  // O^T: lane holds query n, dims 32mb + 8(r/4) + 4hf + r%4
   bf16x8 qf[HD / 16];    // Q^T B operand, k-step s: dims 16s + 8hf .. +7
   bf16x8 pprev[4];       // P^T operands (keys 16u + 8hf .. +7) whose V^T product is still due
+  bf16x8 palt[4];        // the other set of the six-step clean loop (see softmax_pv)
   float m_run;           // running max (log2 units)
   float l_run;           // this half-wave's part of the running denominator
   float c2;              // log2(e) / sqrt(hd)
@@ -181,8 +182,14 @@ struct WaveState {
   // operands pprev): the two are independent, so the vector ALU works while
   // the matrix core runs. The previous product enters O before O is rescaled
   // for this tile's max, so O and l stay at the same reference max.
-  template <bool MASK>
+  // SET selects the probability registers: 0 reads and rewrites pprev (a
+  // copy at the end); in the six-step clean loop, 1 reads pprev and writes
+  // palt, 2 reads palt and writes pprev, so no copy is needed and pprev holds
+  // the due operands again after every six steps.
+  template <bool MASK, int SET = 0>
   __device__ __forceinline__ void softmax_pv(const f32x16& sa, const f32x16& sb, int k0, LdsBytes vprev) {
+    bf16x8(&pin)[4] = SET == 2 ? palt : pprev;
+    bf16x8(&pout)[4] = SET == 1 ? palt : pprev;
     const int hf = lane >> 5;
     // t keeps the raw scores (the max commutes with the positive scale, which
     // is folded into the exponent's FMA), except for ALiBi with a window or
@@ -253,7 +260,7 @@ struct WaveState {
     for (int u = 0; u < 4; ++u)
       pnew[u] = as_bf16x8(make_uint4(pack_bf16x2(t[8 * u + 0], t[8 * u + 1]), pack_bf16x2(t[8 * u + 2], t[8 * u + 3]),
                                      pack_bf16x2(t[8 * u + 4], t[8 * u + 5]), pack_bf16x2(t[8 * u + 6], t[8 * u + 7])));
-    pv(vprev, pprev);
+    pv(vprev, pin);
 #if defined(__HIP_DEVICE_COMPILE__)
     // The probabilities are needed only after the rescale branch below; pin
     // them here so that the compiler does not sink the softmax past the branch
@@ -280,7 +287,7 @@ struct WaveState {
       for (int mb = 0; mb < HD / 32; ++mb) oacc[mb] *= alpha;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pprev[u] = pnew[u];
+    for (int u = 0; u < 4; ++u) pout[u] = pnew[u];
   }
 };
 
@@ -441,9 +448,10 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // first tile, so this starts true (the zero operands of "tile -1" are
   // harmless); with a window a wave may skip the first tiles and starts false.
   bool pending = !WINDOW && !REV;
-  auto step = [&](int kt, auto mask_tag, auto phase_tag) __attribute__((always_inline)) {
+  auto step = [&](int kt, auto mask_tag, auto phase_tag, auto set_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(phase_tag)::value;
+    constexpr int SET = decltype(set_tag)::value;
     unsigned char* cur = P == 0 ? s0 : (P == 1 ? s1 : s2);
     unsigned char* prv = P == 0 ? s2 : (P == 1 ? s0 : s1);
     unsigned char* nxt = P == 0 ? s1 : (P == 1 ? s2 : s0);
@@ -464,7 +472,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       // A wave in its softmax + deferred-product phase gets issue priority
       // over a wave computing scores (measured: fewer cycles per tile).
       __builtin_amdgcn_s_setprio(1);
-      ws.template softmax_pv<MASK>(sa, sb, k0, (LdsBytes)(prv + C::K_BYTES));
+      ws.template softmax_pv<MASK, SET>(sa, sb, k0, (LdsBytes)(prv + C::K_BYTES));
       __builtin_amdgcn_s_setprio(0);
       if constexpr (MASK && (WINDOW || REV)) pending = true;
     } else if (MASK && pending) {
@@ -481,17 +489,20 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
   // Tile kt uses ring stage (kt - kt_begin) % 3, and every loop below starts a
   // round of the ring at stage 0, so each step names its stages statically.
   // Masked rounds run the masked step, which is also correct for clean tiles.
   int kt = kt_begin;
   auto masked_rounds = [&](int end) __attribute__((always_inline)) {
     while (kt < end) {
-      step(kt, M{}, P0{});
+      step(kt, M{}, P0{}, S0{});
       if (++kt >= end) break;
-      step(kt, M{}, P1{});
+      step(kt, M{}, P1{}, S0{});
       if (++kt >= end) break;
-      step(kt, M{}, P2{});
+      step(kt, M{}, P2{}, S0{});
       ++kt;
     }
   };
@@ -505,31 +516,31 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     int i = 0;
     auto masked_rev = [&](int end) __attribute__((always_inline)) {
       while (i < end) {
-        step(nkt - 1 - i, M{}, P0{});
+        step(nkt - 1 - i, M{}, P0{}, S0{});
         if (++i >= end) break;
-        step(nkt - 1 - i, M{}, P1{});
+        step(nkt - 1 - i, M{}, P1{}, S0{});
         if (++i >= end) break;
-        step(nkt - 1 - i, M{}, P2{});
+        step(nkt - 1 - i, M{}, P2{}, S0{});
         ++i;
       }
     };
     masked_rev(mend);
     for (; i + 6 <= total; i += 6) {
-      step(nkt - 1 - i, F{}, P0{});
-      step(nkt - 2 - i, F{}, P1{});
-      step(nkt - 3 - i, F{}, P2{});
-      step(nkt - 4 - i, F{}, P0{});
-      step(nkt - 5 - i, F{}, P1{});
-      step(nkt - 6 - i, F{}, P2{});
+      step(nkt - 1 - i, F{}, P0{}, S1{});
+      step(nkt - 2 - i, F{}, P1{}, S2{});
+      step(nkt - 3 - i, F{}, P2{}, S1{});
+      step(nkt - 4 - i, F{}, P0{}, S2{});
+      step(nkt - 5 - i, F{}, P1{}, S1{});
+      step(nkt - 6 - i, F{}, P2{}, S2{});
     }
     for (; i + 3 <= total; i += 3) {
-      step(nkt - 1 - i, F{}, P0{});
-      step(nkt - 2 - i, F{}, P1{});
-      step(nkt - 3 - i, F{}, P2{});
+      step(nkt - 1 - i, F{}, P0{}, S0{});
+      step(nkt - 2 - i, F{}, P1{}, S0{});
+      step(nkt - 3 - i, F{}, P2{}, S0{});
     }
     // the last one or two clean tiles (the ring is at stage 0 here)
-    if (i < total) step(nkt - 1 - i, F{}, P0{});
-    if (i + 1 < total) step(nkt - 2 - i, F{}, P1{});
+    if (i < total) step(nkt - 1 - i, F{}, P0{}, S0{});
+    if (i + 1 < total) step(nkt - 2 - i, F{}, P1{}, S0{});
     // the last step took tile kt_begin = 0, which every row sees
     pending = true;
   } else {
@@ -545,17 +556,17 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // count the pending probabilities can alternate between two register sets
   // instead of being copied at every step; then three at a time.
   for (; kt + 6 <= kc_hi; kt += 6) {
-    step(kt, F{}, P0{});
-    step(kt + 1, F{}, P1{});
-    step(kt + 2, F{}, P2{});
-    step(kt + 3, F{}, P0{});
-    step(kt + 4, F{}, P1{});
-    step(kt + 5, F{}, P2{});
+    step(kt, F{}, P0{}, S1{});
+    step(kt + 1, F{}, P1{}, S2{});
+    step(kt + 2, F{}, P2{}, S1{});
+    step(kt + 3, F{}, P0{}, S2{});
+    step(kt + 4, F{}, P1{}, S1{});
+    step(kt + 5, F{}, P2{}, S2{});
   }
   for (; kt + 3 <= kc_hi; kt += 3) {
-    step(kt, F{}, P0{});
-    step(kt + 1, F{}, P1{});
-    step(kt + 2, F{}, P2{});
+    step(kt, F{}, P0{}, S0{});
+    step(kt + 1, F{}, P1{}, S0{});
+    step(kt + 2, F{}, P2{}, S0{});
   }
   masked_rounds(nkt);
   }
