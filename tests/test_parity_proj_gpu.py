@@ -168,6 +168,32 @@ def test_block_composition_matches_oracle():
     assert err <= 1e-2, err
 
 
+@pytest.mark.timeout(900)
+def test_block_full_size_fp32_output():
+    """The Llama-3-8B block exactly as bench.py runs it (B=4, T=4096, D=4096, H=32, KV=8, hd=128,
+    RoPE 5e5; projection, causal attention with the rotation off and bf16 output, output
+    projection) but with an fp32 block output, against the oracle's block on every element of
+    sequence 0 (all 4096 rows: under the causal mask a row depends only on the tokens up to it)."""
+    pw = W.PROJ_LLAMA3_8B
+    inp = W.proj_inputs(pw)
+    print(f"[block full size] {pw.name}", flush=True)
+    q, k, v = bd.qkv_proj(inp.x.cuda(), inp.w_qkv.cuda(), pw.H, pw.KV, rope_base=pw.rope_base)
+    out, _ = bd.prefill(q, k, v, rope_base=0.0, causal=True, out_dtype=torch.bfloat16)
+    del q, k, v
+    y = bd.out_proj(out, inp.w_o.cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = to64(y[0:1])
+    del y, out
+    rq, rk, rv = qkv_projection(to64(inp.x[0:1]), to64(inp.w_qkv), H=pw.H, KV=pw.KV, hd=pw.hd,
+                                rope_base=pw.rope_base)
+    ro, _ = attention_prefill(rq, rk, rv, rope_base=0.0, causal=True)
+    ry = out_projection(ro, to64(inp.w_o))
+    err = np.abs(got - ry).max()
+    print(f"  every element of sequence 0: max abs err {err:.3g}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= 1e-2, err
+
+
 def test_decode_step_with_projected_cache():
     """A decode step built from the projection: attn_qkv_proj_cache_fwd writes the new token's
     rotated key and value into slot L and returns its rotated query; attn_decode_fwd then runs
