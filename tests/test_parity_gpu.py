@@ -161,6 +161,41 @@ def test_prefill_chunk_and_window(shape, dtype):
                   label="chunk/window")
 
 
+ALIBI_CHUNKS = [
+    # B, Tq, Tk, H, KV, hd, q_offset, alibi: causal ALiBi chunks with no window (the instance that walks its
+    # key tiles from the diagonal down and takes the in-tile bias from the matrix core)
+    (2, 200, 700, 8, 2, 128, 500, 1),      # last chunk, GQA
+    (1, 250, 900, 4, 4, 128, 100, 2),      # MHA: 256-row query blocks, a chunk starting mid-block
+    (1, 1, 513, 8, 8, 64, 512, 1),         # a one-token chunk
+    (1, 333, 1000, 16, 16, 128, 667, 1),   # the last 333 tokens, MHA, 16 heads
+]
+# (the steeper slope family on that 16-head shape concentrates rows on two or three keys, where the bf16
+# rounding of the rotated q and k and of the probabilities reaches ~0.012 against the fp64 oracle:
+# the path's error budget, not this walk order; the 4-head case above takes that family)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", ALIBI_CHUNKS, ids=lambda c: "B%dTq%dTk%dH%dKV%dhd%d_off%d_a%d" % c)
+def test_prefill_alibi_chunks(shape, dtype):
+    B, Tq, Tk, H, KV, hd, off, alibi = shape
+    q, k, v = W.random_prefill(3000 + Tk + off, B, Tk, H, KV, hd, "bf16" if dtype == torch.bfloat16 else "f32")
+    q = q[:, :, off:off + Tq].contiguous()
+    check_prefill(q, k, v, pos0=3, rope_base=10000.0, alibi=alibi, q_offset=off, label="alibi chunk")
+
+
+def test_chunked_alibi_prefill_equals_full_prefill_bitwise():
+    """Causal ALiBi processed chunk by chunk gives the full call's rows bit for bit: every row meets
+    the same tiles in the same order (from its own tile down), the fully masked ones adding exact zeros."""
+    B, T, H, KV, hd = 1, 640, 8, 8, 128
+    q, k, v = W.random_prefill(78, B, T, H, KV, hd)
+    full, full_lse = gpu_prefill(q, k, v, rope_base=10000.0, alibi=1)
+    for start, stop in [(0, 100), (100, 357), (357, 640)]:
+        part, part_lse = gpu_prefill(q[:, :, start:stop].contiguous(), k[:, :, :stop].contiguous(),
+                                     v[:, :, :stop].contiguous(), rope_base=10000.0, alibi=1, q_offset=start)
+        assert torch.equal(part, full[:, :, start:stop]), (start, stop)
+        assert torch.equal(part_lse, full_lse[:, :, start:stop])
+
+
 def test_chunked_prefill_equals_full_prefill_bitwise():
     """Processing the prompt in chunks gives the full call's rows bit for bit (bf16, GQA, window)."""
     B, T, H, KV, hd = 1, 640, 8, 2, 128
