@@ -61,6 +61,14 @@ def check_prefill(q, k, v, pos0=0, rope_base=10000.0, causal=True, alibi=0, labe
     return err
 
 
+@pytest.fixture(params=["8", "4"], ids=["8waves", "4waves"])
+def waves(request, monkeypatch):
+    """Force the prefill kernel's workgroup size (8 or 4 waves; left to itself the library takes 4 waves
+    only for grids that would not give every compute unit a workgroup)."""
+    monkeypatch.setenv("ATTN_PREFILL_WAVES", request.param)
+    return request.param
+
+
 # ------------------------------------------------------------- the lab instance
 @pytest.mark.parametrize("pos0", [0, 100])
 def test_tiny_fp32_lab_instance(pos0):
@@ -113,7 +121,7 @@ SHAPES = [
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dT%dH%dKV%dhd%d" % s)
-def test_prefill_shapes(shape, dtype):
+def test_prefill_shapes(shape, dtype, waves):
     B, T, H, KV, hd = shape
     q, k, v = W.random_prefill(1000 + T, B, T, H, KV, hd, "bf16" if dtype == torch.bfloat16 else "f32")
     check_prefill(q, k, v, pos0=3, rope_base=10000.0, label=str(shape))
@@ -132,7 +140,7 @@ FLAGS = [
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("flags", FLAGS, ids=lambda f: "c%d_a%d_b%g_p%d" % f)
-def test_prefill_flags(flags, dtype):
+def test_prefill_flags(flags, dtype, waves):
     causal, alibi, base, pos0 = flags
     q, k, v = W.random_prefill(7, 2, 190, 8, 2, 128, "bf16" if dtype == torch.bfloat16 else "f32")
     check_prefill(q, k, v, pos0=pos0, rope_base=base, causal=causal, alibi=alibi, label="flags")
@@ -153,7 +161,7 @@ CHUNKS = [
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shape", CHUNKS, ids=lambda c: "B%dTq%dTk%dH%dKV%dhd%d_off%d_w%d" % c)
-def test_prefill_chunk_and_window(shape, dtype):
+def test_prefill_chunk_and_window(shape, dtype, waves):
     B, Tq, Tk, H, KV, hd, off, win = shape
     q, k, v = W.random_prefill(2000 + Tk + win, B, Tk, H, KV, hd, "bf16" if dtype == torch.bfloat16 else "f32")
     q = q[:, :, off:off + Tq].contiguous()
@@ -176,11 +184,33 @@ ALIBI_CHUNKS = [
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shape", ALIBI_CHUNKS, ids=lambda c: "B%dTq%dTk%dH%dKV%dhd%d_off%d_a%d" % c)
-def test_prefill_alibi_chunks(shape, dtype):
+def test_prefill_alibi_chunks(shape, dtype, waves):
     B, Tq, Tk, H, KV, hd, off, alibi = shape
     q, k, v = W.random_prefill(3000 + Tk + off, B, Tk, H, KV, hd, "bf16" if dtype == torch.bfloat16 else "f32")
     q = q[:, :, off:off + Tq].contiguous()
     check_prefill(q, k, v, pos0=3, rope_base=10000.0, alibi=alibi, q_offset=off, label="alibi chunk")
+
+
+@pytest.mark.parametrize("case", [
+    # B, Tq, Tk, H, KV, hd, q_offset, window, alibi, rope_base
+    (2, 700, 700, 8, 2, 128, 0, 0, 0, 10000.0),     # GQA, several query blocks
+    (1, 900, 900, 4, 4, 128, 0, 0, 1, 0.0),         # causal ALiBi walked from the diagonal down
+    (1, 333, 1000, 8, 2, 128, 600, 257, 0, 5e5),    # chunk with a sliding window
+    (1, 512, 512, 8, 2, 64, 0, 0, 2, 10000.0),      # hd 64, steep slopes
+], ids=lambda c: "B%dTq%dTk%dH%dKV%dhd%d_off%d_w%d_a%d_b%g" % c)
+def test_four_and_eight_wave_workgroups_agree_bitwise(case, monkeypatch):
+    """The 4-wave and 8-wave workgroups give every row the same tiles in the same order with the same
+    arithmetic, so their outputs agree bit for bit."""
+    B, Tq, Tk, H, KV, hd, off, win, alibi, base = case
+    q, k, v = W.random_prefill(4000 + Tk + off, B, Tk, H, KV, hd)
+    q = q[:, :, off:off + Tq].contiguous()
+    res = {}
+    for w in ("8", "4"):
+        monkeypatch.setenv("ATTN_PREFILL_WAVES", w)
+        res[w] = gpu_prefill(q, k, v, rope_base=base, alibi=alibi, q_offset=off, window=win,
+                             out_dtype=torch.bfloat16)
+    assert torch.equal(res["8"][0], res["4"][0])
+    assert torch.equal(res["8"][1], res["4"][1])
 
 
 def test_chunked_alibi_prefill_equals_full_prefill_bitwise():

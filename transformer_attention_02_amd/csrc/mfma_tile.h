@@ -145,8 +145,9 @@ struct Dma {
     }
   }
 
-  __device__ __forceinline__ void issue(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, unsigned char* stage,
-                                        int wave) const {
+  // Tile kt of both tensors, the first into kdst and the second into vdst.
+  __device__ __forceinline__ void issue(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, unsigned char* kdst,
+                                        unsigned char* vdst, int wave) const {
     const int bytes = (T - kt * BN) * HD * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (long)kt * BN * HD, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (long)kt * BN * HD, bytes);
@@ -154,10 +155,15 @@ struct Dma {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;
 #if defined(__HIP_DEVICE_COMPILE__)  // (the host pass drops the kernel stubs of later instantiations otherwise)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(stage + 1024 * q), 16, koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(stage + C::K_BYTES + 1024 * q), 16, voff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(kdst + 1024 * q), 16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(vdst + 1024 * q), 16, voff[i], 0, 0, 0);
 #endif
     }
+  }
+  // Both tiles into one stage: the first tensor, then the second.
+  __device__ __forceinline__ void issue(const uint16_t* Kg, const uint16_t* Vg, int kt, int T, unsigned char* stage,
+                                        int wave) const {
+    issue(Kg, Vg, kt, T, stage, stage + C::K_BYTES, wave);
   }
 };
 

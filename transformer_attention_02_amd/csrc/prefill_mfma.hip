@@ -8,7 +8,10 @@
 // Work decomposition
 //   * A workgroup is 8 waves (two per SIMD). It owns one block of query rows
 //     for up to 4 query heads that share one key/value head (grouped-query
-//     packing), so every K/V tile staged in LDS serves 256 query rows.
+//     packing), so every K/V tile staged in LDS serves 256 query rows. A grid
+//     that would not give every compute unit a workgroup runs 4-wave
+//     workgroups instead (half the rows each, 80 KiB of LDS, two per compute
+//     unit): twice as many workgroups share out the same work.
 //   * A wave owns 32 query rows of one head and computes S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16. In the 32x32 accumulator a lane holds one
 //     query (column) and 16 keys (rows), so the row max and row sum are
@@ -44,15 +47,13 @@ namespace {
 
 using namespace tile;
 
-constexpr int NW = 8;   // waves per workgroup (two per SIMD)
 constexpr int kKAhead = 4;       // K operand reads issued ahead of the score MFMAs
 constexpr int kValuPerMfma = 8;  // softmax instructions issued per deferred V^T MFMA
-constexpr int NT = NW * 64;
 
 struct GridMap {
   int hpw;       // heads per workgroup (1, 2 or 4)
   int hchunks;   // group / hpw
-  int bm;        // query rows per head per workgroup = 32 * (NW / hpw)
+  int bm;        // query rows per head per workgroup = 32 * (waves / hpw)
   int nqb;       // query blocks
   int units;     // B * KV * hchunks
   int xcd_aware;
@@ -291,18 +292,30 @@ struct WaveState {
   }
 };
 
-template <int HD, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// LDS buffer I of one kernel instance: with 8 waves, stage I of K then V;
+// with 4 waves, K buffer I (I = 0, 1) or V buffer I - 2 (I = 2, 3, 4).
+template <int HD, int NW, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW, int I>
+__device__ __forceinline__ unsigned char* lds_buf() {
+  __shared__ __attribute__((aligned(16))) unsigned char b[NW == 8 ? Cfg<HD>::STAGE : Cfg<HD>::K_BYTES];
+  return b;
+}
+
+template <int HD, int NW, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using C = Cfg<HD>;
-  // Three stage buffers, each its own LDS object: stage kt%3 holds tile kt
-  // (K then V), stage (kt+1)%3 receives tile kt+1 by DMA, stage (kt-1)%3 still
-  // holds V of tile kt-1 for its deferred V^T product. As separate objects the
-  // compiler can tell that the DMA into one stage cannot alias the reads of
-  // another, and does not wait for the in-flight tile before reading.
-  __shared__ __attribute__((aligned(16))) unsigned char s0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char s1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char s2[C::STAGE];
+  constexpr int NT = NW * 64;
+  // Each buffer is its own LDS object, so the compiler can tell that the DMA
+  // into one cannot alias the reads of another, and does not wait for the
+  // in-flight tile before reading.
+  //  * 8 waves: three stages of K then V; stage j%3 holds walk tile j, stage
+  //    (j+1)%3 receives tile j+1 by DMA, stage (j-1)%3 still holds V of tile
+  //    j-1 for its deferred V^T product.
+  //  * 4 waves: K of tile j in kb[j%2] (read in step j), V in vb[j%3] (read in
+  //    step j+1); 80 KiB in all, so two workgroups share a compute unit.
+  static_assert(NW == 8 || NW == 4, "8- or 4-wave workgroups");
+  static_assert(C::K_BYTES == C::V_BYTES, "K and V buffers are interchangeable");
+#define LB(I) (lds_buf<HD, NW, ALIBI, CAUSAL, OUT_BF16, WINDOW, (I)>())
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -358,14 +371,22 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // O on most steps). Other variants walk upwards; the online softmax gives
   // the same result in any order, up to rounding.
   constexpr bool REV = ALIBI && CAUSAL && !WINDOW;
-  // The first K/V tile streams into stage 0 during the Q set-up.
+  // K and V of walk tile j: where they sit (P = j % 6)
+  auto kbuf = [&](int P) __attribute__((always_inline)) {
+    return NW == 8 ? (P % 3 == 0 ? LB(0) : (P % 3 == 1 ? LB(1) : LB(2))) : (P % 2 == 0 ? LB(0) : LB(1));
+  };
+  auto vbuf = [&](int P) __attribute__((always_inline)) {
+    return NW == 8 ? (P % 3 == 0 ? LB(0) : (P % 3 == 1 ? LB(1) : LB(2))) + C::K_BYTES
+                   : (P % 3 == 0 ? LB(2) : (P % 3 == 1 ? LB(3) : LB(4)));
+  };
+  // The first K/V tile streams in during the Q set-up.
   Dma<HD, NW> dma;
   dma.init(wave, lane);
-  dma.issue(Kg, Vg, REV ? nkt - 1 : kt_begin, a.Tk, s0, wave);
-  // Stage 2 stands in for the tile before the first one: its V part is zeroed
-  // and the pending probabilities start at zero, so the first tile's deferred
-  // product adds exact zeros.
-  for (int e = tid; e < C::V_BYTES / 16; e += NT) reinterpret_cast<uint4*>(s2 + C::K_BYTES)[e] = make_uint4(0, 0, 0, 0);
+  dma.issue(Kg, Vg, REV ? nkt - 1 : kt_begin, a.Tk, kbuf(0), vbuf(0), wave);
+  // V of the tile before the first one (buffer 2) is zeroed and the pending
+  // probabilities start at zero, so the first tile's deferred product adds
+  // exact zeros.
+  for (int e = tid; e < C::V_BYTES / 16; e += NT) reinterpret_cast<uint4*>(vbuf(2))[e] = make_uint4(0, 0, 0, 0);
 
   WaveState<HD, ALIBI, CAUSAL, WINDOW> ws;
   ws.qi = a.q_off + qw0 + n;
@@ -384,12 +405,12 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   for (int u = 0; u < 4; ++u) ws.pprev[u] = as_bf16x8(make_uint4(0, 0, 0, 0));
 
   // ---- Q rows -> B operands (rotated in fp32, rounded to bf16). When it fits
-  // in stage 1, the rotary cos/sin of the workgroup's bm rows are computed once
-  // (layout [pair][row], so lanes reading consecutive rows hit distinct banks)
-  // and shared by the waves of all heads in the workgroup.
+  // in the K buffer of tile 1, the rotary cos/sin of the workgroup's bm rows
+  // are computed once (layout [pair][row], so lanes reading consecutive rows
+  // hit distinct banks) and shared by the waves of all heads in the workgroup.
   {
-    const bool table = a.rope && (HD / 2) * gm.bm * (int)sizeof(float2) <= C::STAGE;
-    float2* cs = reinterpret_cast<float2*>(s1);  // [HD/2][bm]
+    const bool table = a.rope && (HD / 2) * gm.bm * (int)sizeof(float2) <= (NW == 8 ? C::STAGE : C::K_BYTES);
+    float2* cs = reinterpret_cast<float2*>(kbuf(1));  // [HD/2][bm]
     if (table) {
       for (int e = tid; e < (HD / 2) * gm.bm; e += NT) {
         const int r = e % gm.bm, p = e / gm.bm;
@@ -432,7 +453,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       for (int s = 0; s < HD / 16; ++s) ws.qf[s] = rotate(raw[s], qr, 8 * s + 4 * hf);
     }
   }
-  // Tile 0 has landed, stage 2 is zeroed and no wave still reads the table (stage 1).
+  // Tile 0 has landed, V buffer 2 is zeroed and no wave still reads the table.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -450,16 +471,15 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   bool pending = !WINDOW && !REV;
   auto step = [&](int kt, auto mask_tag, auto phase_tag, auto set_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int P = decltype(phase_tag)::value;
+    constexpr int P = decltype(phase_tag)::value;  // walk step % 6
     constexpr int SET = decltype(set_tag)::value;
-    unsigned char* cur = P == 0 ? s0 : (P == 1 ? s1 : s2);
-    unsigned char* prv = P == 0 ? s2 : (P == 1 ? s0 : s1);
-    unsigned char* nxt = P == 0 ? s1 : (P == 1 ? s2 : s0);
+    unsigned char* cur = kbuf(P);
+    unsigned char* prv = vbuf(P + 5);
     const int k0 = kt * BN;
     if constexpr (REV) {
-      if (kt > kt_begin) dma.issue(Kg, Vg, kt - 1, a.Tk, nxt, wave);
+      if (kt > kt_begin) dma.issue(Kg, Vg, kt - 1, a.Tk, kbuf(P + 1), vbuf(P + 1), wave);
     } else {
-      if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.Tk, nxt, wave);
+      if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.Tk, kbuf(P + 1), vbuf(P + 1), wave);
     }
     // in a masked tile a wave may be past its last visible key (causal) or
     // before its first one (sliding window)
@@ -472,13 +492,13 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       // A wave in its softmax + deferred-product phase gets issue priority
       // over a wave computing scores (measured: fewer cycles per tile).
       __builtin_amdgcn_s_setprio(1);
-      ws.template softmax_pv<MASK, SET>(sa, sb, k0, (LdsBytes)(prv + C::K_BYTES));
+      ws.template softmax_pv<MASK, SET>(sa, sb, k0, (LdsBytes)prv);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (MASK && (WINDOW || REV)) pending = true;
     } else if (MASK && pending) {
       // past the wave's last visible key: settle the owed product (the wave
       // does not run again)
-      ws.pv((LdsBytes)(prv + C::K_BYTES), ws.pprev);
+      ws.pv((LdsBytes)prv, ws.pprev);
       pending = false;
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -489,12 +509,17 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using P4 = std::integral_constant<int, 4>;
+  using P5 = std::integral_constant<int, 5>;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  // Tile kt uses ring stage (kt - kt_begin) % 3, and every loop below starts a
-  // round of the ring at stage 0, so each step names its stages statically.
-  // Masked rounds run the masked step, which is also correct for clean tiles.
+  // Walk step j uses the buffers named by j % 6 (the rings turn every 3
+  // steps with 8 waves, every 6 with 4), and every loop below starts a round
+  // of R steps at 0, so each step names its buffers statically. Masked rounds
+  // run the masked step, which is also correct for clean tiles.
+  constexpr int R = NW == 8 ? 3 : 6;
   int kt = kt_begin;
   auto masked_rounds = [&](int end) __attribute__((always_inline)) {
     while (kt < end) {
@@ -503,6 +528,14 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       step(kt, M{}, P1{}, S0{});
       if (++kt >= end) break;
       step(kt, M{}, P2{}, S0{});
+      if constexpr (NW == 4) {
+        if (++kt >= end) break;
+        step(kt, M{}, P3{}, S0{});
+        if (++kt >= end) break;
+        step(kt, M{}, P4{}, S0{});
+        if (++kt >= end) break;
+        step(kt, M{}, P5{}, S0{});
+      }
       ++kt;
     }
   };
@@ -512,7 +545,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     // masked runs masked), then the clean tiles. A wave skips the masked tiles
     // past its last token and runs every tile from its first visible one on.
     const int total = nkt - kt_begin;
-    const int mend = min(total, (nkt - kc_hi + 2) / 3 * 3);
+    const int mend = min(total, (nkt - kc_hi + R - 1) / R * R);
     int i = 0;
     auto masked_rev = [&](int end) __attribute__((always_inline)) {
       while (i < end) {
@@ -521,6 +554,14 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
         step(nkt - 1 - i, M{}, P1{}, S0{});
         if (++i >= end) break;
         step(nkt - 1 - i, M{}, P2{}, S0{});
+        if constexpr (NW == 4) {
+          if (++i >= end) break;
+          step(nkt - 1 - i, M{}, P3{}, S0{});
+          if (++i >= end) break;
+          step(nkt - 1 - i, M{}, P4{}, S0{});
+          if (++i >= end) break;
+          step(nkt - 1 - i, M{}, P5{}, S0{});
+        }
         ++i;
       }
     };
@@ -529,28 +570,35 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       step(nkt - 1 - i, F{}, P0{}, S1{});
       step(nkt - 2 - i, F{}, P1{}, S2{});
       step(nkt - 3 - i, F{}, P2{}, S1{});
-      step(nkt - 4 - i, F{}, P0{}, S2{});
-      step(nkt - 5 - i, F{}, P1{}, S1{});
-      step(nkt - 6 - i, F{}, P2{}, S2{});
+      step(nkt - 4 - i, F{}, P3{}, S2{});
+      step(nkt - 5 - i, F{}, P4{}, S1{});
+      step(nkt - 6 - i, F{}, P5{}, S2{});
     }
-    for (; i + 3 <= total; i += 3) {
-      step(nkt - 1 - i, F{}, P0{}, S0{});
-      step(nkt - 2 - i, F{}, P1{}, S0{});
-      step(nkt - 3 - i, F{}, P2{}, S0{});
+    if constexpr (NW == 8) {
+      for (; i + 3 <= total; i += 3) {
+        step(nkt - 1 - i, F{}, P0{}, S0{});
+        step(nkt - 2 - i, F{}, P1{}, S0{});
+        step(nkt - 3 - i, F{}, P2{}, S0{});
+      }
     }
-    // the last one or two clean tiles (the ring is at stage 0 here)
+    // the last clean tiles, fewer than a round (the rounds are at 0 here)
     if (i < total) step(nkt - 1 - i, F{}, P0{}, S0{});
     if (i + 1 < total) step(nkt - 2 - i, F{}, P1{}, S0{});
+    if constexpr (NW == 4) {
+      if (i + 2 < total) step(nkt - 3 - i, F{}, P2{}, S0{});
+      if (i + 3 < total) step(nkt - 4 - i, F{}, P3{}, S0{});
+      if (i + 4 < total) step(nkt - 5 - i, F{}, P4{}, S0{});
+    }
     // the last step took tile kt_begin = 0, which every row sees
     pending = true;
   } else {
   if constexpr (WINDOW) {
     // tiles at the window's start, up to the first round boundary at or after
     // the first clean tile
-    masked_rounds(min(nkt, kt_begin + (kc_lo - kt_begin + 2) / 3 * 3));
+    masked_rounds(min(nkt, kt_begin + (kc_lo - kt_begin + R - 1) / R * R));
   }
   if constexpr (WINDOW) {
-    if (kt + 3 <= kc_hi) pending = true;  // every active wave runs a clean tile
+    if (kt + R <= kc_hi) pending = true;  // every active wave runs a clean tile
   }
   // Clean tiles six per iteration (two turns of the ring): with an even step
   // count the pending probabilities can alternate between two register sets
@@ -559,33 +607,33 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     step(kt, F{}, P0{}, S1{});
     step(kt + 1, F{}, P1{}, S2{});
     step(kt + 2, F{}, P2{}, S1{});
-    step(kt + 3, F{}, P0{}, S2{});
-    step(kt + 4, F{}, P1{}, S1{});
-    step(kt + 5, F{}, P2{}, S2{});
+    step(kt + 3, F{}, P3{}, S2{});
+    step(kt + 4, F{}, P4{}, S1{});
+    step(kt + 5, F{}, P5{}, S2{});
   }
-  for (; kt + 3 <= kc_hi; kt += 3) {
-    step(kt, F{}, P0{}, S0{});
-    step(kt + 1, F{}, P1{}, S0{});
-    step(kt + 2, F{}, P2{}, S0{});
+  if constexpr (NW == 8) {
+    for (; kt + 3 <= kc_hi; kt += 3) {
+      step(kt, F{}, P0{}, S0{});
+      step(kt + 1, F{}, P1{}, S0{});
+      step(kt + 2, F{}, P2{}, S0{});
+    }
   }
   masked_rounds(nkt);
   }
   if (!wave_active) return;
   // the last tile's V^T product (no DMA is in flight any more)
-  if (pending) {
-    const int p = (nkt - 1 - kt_begin) % 3;
-    ws.pv((LdsBytes)((p == 0 ? s0 : (p == 1 ? s1 : s2)) + C::K_BYTES), ws.pprev);
-  }
+  if (pending) ws.pv((LdsBytes)vbuf((nkt - 1 - kt_begin) % 3), ws.pprev);
 
   const float l_tot = ws.l_run + xhalf(ws.l_run);
   const float inv_l = 1.0f / l_tot;
   if constexpr (OUT_BF16) {
     // bf16 O leaves through LDS so that every store instruction writes whole
     // rows: the wave puts its 32 rows, in the accumulator layout, into a
-    // private slot (a quarter of one of the two ring stages the last tile does
-    // not occupy; no wave reads those any more and no DMA is in flight), then
-    // reads them back row-major. 16-byte chunks are XOR-swizzled by row, so
-    // neither side has bank conflicts.
+    // private slot (8 waves: a quarter of one of the two ring stages the last
+    // tile does not occupy; 4 waves: half of a K buffer; no wave reads those
+    // any more and no DMA is in flight), then reads them back row-major.
+    // 16-byte chunks are XOR-swizzled by row, so neither side has bank
+    // conflicts.
     constexpr int RB = 2 * HD;    // bytes of one output row
     constexpr int CPR = RB / 16;  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR; // rows per read-back instruction
@@ -594,9 +642,14 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     int el = lane;
     asm volatile("" : "+v"(el));
     const int en = el & 31, ehf = el >> 5;
-    const int p_last = (nkt - 1 - kt_begin) % 3;
-    unsigned char* fs = (wave < 4) ? (p_last == 0 ? s1 : s0) : (p_last == 2 ? s1 : s2);
-    LDS unsigned char* slot = (LDS unsigned char*)(fs + (wave & 3) * (C::STAGE / 4));
+    LDS unsigned char* slot;
+    if constexpr (NW == 8) {
+      const int p_last = (nkt - 1 - kt_begin) % 3;
+      unsigned char* fs = (wave < 4) ? (p_last == 0 ? LB(1) : LB(0)) : (p_last == 2 ? LB(1) : LB(2));
+      slot = (LDS unsigned char*)(fs + (wave & 3) * (C::STAGE / 4));
+    } else {
+      slot = (LDS unsigned char*)(kbuf(wave >> 1) + (wave & 1) * (C::K_BYTES / 2));
+    }
 #pragma unroll
     for (int mb = 0; mb < HD / 32; ++mb) {
 #pragma unroll
@@ -639,13 +692,14 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   const int qi = qw0 + n;  // query row
   if (qi >= a.Tq) return;
   if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.Tq + qi] = (ws.m_run + log2f(l_tot)) * 0.69314718055994531f;
+#undef LB
 }
 
-GridMap make_grid(const PrefillArgs& a) {
+GridMap make_grid(const PrefillArgs& a, int nw) {
   GridMap gm;
   gm.hpw = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
   gm.hchunks = a.group / gm.hpw;
-  gm.bm = 32 * (NW / gm.hpw);
+  gm.bm = 32 * (nw / gm.hpw);
   gm.nqb = (a.Tq + gm.bm - 1) / gm.bm;
   gm.units = a.B * a.KV * gm.hchunks;
   gm.xcd_aware = (gm.units % 8) == 0;
@@ -659,28 +713,51 @@ GridMap make_grid(const PrefillArgs& a) {
   return gm;
 }
 
-template <int HD, bool ALIBI, bool CAUSAL, bool WINDOW>
+template <int HD, int NW, bool ALIBI, bool CAUSAL, bool WINDOW>
 void launch_out(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
   if (a.out_bf16) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, true, WINDOW>), grid, dim3(NT), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, NW, ALIBI, CAUSAL, true, WINDOW>), grid, dim3(NW * 64), 0, s, a, gm);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, ALIBI, CAUSAL, false, WINDOW>), grid, dim3(NT), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, NW, ALIBI, CAUSAL, false, WINDOW>), grid, dim3(NW * 64), 0, s, a, gm);
   }
 }
 
 // The sliding window is a separate instance (causal only), so the plain
 // kernels carry none of its masking or tile-skipping code.
-template <int HD>
+template <int HD, int NW>
 void launch_hd(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
   if (a.alibi) {
-    if (a.window > 0) launch_out<HD, true, true, true>(a, gm, grid, s);
-    else if (a.causal) launch_out<HD, true, true, false>(a, gm, grid, s);
-    else launch_out<HD, true, false, false>(a, gm, grid, s);
+    if (a.window > 0) launch_out<HD, NW, true, true, true>(a, gm, grid, s);
+    else if (a.causal) launch_out<HD, NW, true, true, false>(a, gm, grid, s);
+    else launch_out<HD, NW, true, false, false>(a, gm, grid, s);
   } else {
-    if (a.window > 0) launch_out<HD, false, true, true>(a, gm, grid, s);
-    else if (a.causal) launch_out<HD, false, true, false>(a, gm, grid, s);
-    else launch_out<HD, false, false, false>(a, gm, grid, s);
+    if (a.window > 0) launch_out<HD, NW, false, true, true>(a, gm, grid, s);
+    else if (a.causal) launch_out<HD, NW, false, true, false>(a, gm, grid, s);
+    else launch_out<HD, NW, false, false, false>(a, gm, grid, s);
   }
+}
+
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Waves per workgroup: 8 unless the 8-wave grid leaves compute units without
+// a workgroup. ATTN_PREFILL_WAVES=4 or 8 forces one (for tests).
+int pick_waves(const PrefillArgs& a) {
+  if (const char* e = getenv("ATTN_PREFILL_WAVES")) {
+    if (e[0] == '4' && e[1] == 0) return 4;
+    if (e[0] == '8' && e[1] == 0) return 8;
+  }
+  const GridMap gm = make_grid(a, 8);
+  return (long)gm.units * gm.nqb < device_cus() ? 4 : 8;
 }
 
 }  // namespace
@@ -688,17 +765,20 @@ void launch_hd(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s
 bool prefill_mfma_supported(const PrefillArgs& a, int bf16) {
   if (!bf16 || (a.hd != 64 && a.hd != 128)) return false;
   if ((long)a.Tk * a.hd * 2 >= (1L << 31)) return false;  // buffer descriptors hold 32-bit sizes
-  const GridMap gm = make_grid(a);
+  const GridMap gm = make_grid(a, 4);  // (the 4-wave grid is the larger one)
   return (long)gm.units * gm.nqb < (1L << 31);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
-  const GridMap gm = make_grid(a);
+  const int nw = pick_waves(a);
+  const GridMap gm = make_grid(a, nw);
   const dim3 grid((unsigned)(gm.units * gm.nqb));
   if (a.hd == 128) {
-    launch_hd<128>(a, gm, grid, s);
+    if (nw == 8) launch_hd<128, 8>(a, gm, grid, s);
+    else launch_hd<128, 4>(a, gm, grid, s);
   } else {
-    launch_hd<64>(a, gm, grid, s);
+    if (nw == 8) launch_hd<64, 8>(a, gm, grid, s);
+    else launch_hd<64, 4>(a, gm, grid, s);
   }
   return hipGetLastError();
 }
