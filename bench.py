@@ -430,7 +430,8 @@ def measure_ceilings(torch, dev, mfma, hbm):
         e1.record()
         torch.cuda.synchronize()
         res["hbm_read_stream_gbs"] = nb / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
-        res["hbm_read_stream"] = "read-only stream of 4 GiB, non-temporal 16-byte loads (libattn_probe.so)"
+        res["hbm_read_stream"] = ("read-only stream of 4 GiB, non-temporal 16-byte loads, 16384 x 512 threads, 8 loads in "
+                                  "flight per thread (libattn_probe.so)")
         y_ = torch.empty(1 << 30, dtype=torch.bfloat16, device=dev)
         src = x_[: y_.numel()]
         for _ in range(3):
