@@ -409,13 +409,34 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // are computed once (layout [pair][row], so lanes reading consecutive rows
   // hit distinct banks) and shared by the waves of all heads in the workgroup.
   {
-    const bool table = a.rope && (HD / 2) * gm.bm * (int)sizeof(float2) <= (NW == 8 ? C::STAGE : C::K_BYTES);
+    const int qr = qw0 + n;  // query row
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                      (((long)b * a.H + head) * a.Tq + min(qr, a.Tq - 1)) * HD);
+    uint4 raw[HD / 16];
+    // 4-wave workgroups (small grids, one wave per SIMD) request their Q rows
+    // before the table, so the two latencies overlap; with 8 waves the second
+    // wave of each SIMD covers it, and the early loads measured slower there.
+    if constexpr (NW == 4) {
+#pragma unroll
+      for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
+    }
+    // The table fits only with 4 heads per workgroup (bm = 8 * NW rows), so a
+    // thread fills HD / 16 entries, pairs tid / bm + 8i; their frequencies are
+    // all requested before the first is used (one memory latency, not HD / 16).
+    constexpr int TBM = 8 * NW;
+    constexpr int TPT = (HD / 2) * TBM / NT;
+    static_assert((HD / 2) * TBM * sizeof(float2) <= (NW == 8 ? C::STAGE : C::K_BYTES), "table fits");
+    const bool table = a.rope && gm.bm == TBM;
     float2* cs = reinterpret_cast<float2*>(kbuf(1));  // [HD/2][bm]
     if (table) {
-      for (int e = tid; e < (HD / 2) * gm.bm; e += NT) {
-        const int r = e % gm.bm, p = e / gm.bm;
+      double fr[TPT];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) fr[i] = a.freqs.rev[(tid + i * NT) / TBM];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int e = tid + i * NT;
         float c, sn;
-        rope_cos_sin(a.pos0 + tq0 + r, a.freqs.rev[p], c, sn);
+        rope_cos_sin(a.pos0 + tq0 + e % TBM, fr[i], c, sn);
         cs[e] = make_float2(c, sn);
       }
       __syncthreads();
@@ -439,12 +460,10 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       }
       return as_bf16x8(make_uint4(d[0], d[1], d[2], d[3]));
     };
-    const int qr = qw0 + n;  // query row
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                      (((long)b * a.H + head) * a.Tq + min(qr, a.Tq - 1)) * HD);
-    uint4 raw[HD / 16];
+    if constexpr (NW == 8) {
 #pragma unroll
-    for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
+      for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
+    }
     if (!a.rope) {
 #pragma unroll
       for (int s = 0; s < HD / 16; ++s) ws.qf[s] = as_bf16x8(raw[s]);
