@@ -61,11 +61,18 @@ def check_prefill(q, k, v, pos0=0, rope_base=10000.0, causal=True, alibi=0, labe
     return err
 
 
-@pytest.fixture(params=["8", "4"], ids=["8waves", "4waves"])
+@pytest.fixture(params=["8", "4", "ws"], ids=["8waves", "4waves", "wavesplit"])
 def waves(request, monkeypatch):
-    """Force the prefill kernel's workgroup size (8 or 4 waves; left to itself the library takes 4 waves
-    only for grids that would not give every compute unit a workgroup)."""
-    monkeypatch.setenv("ATTN_PREFILL_WAVES", request.param)
+    """Force the prefill kernel's workgroups: 8 waves, 4 waves, or 4 waves that split one 32-row block's key
+    tiles four ways (head size 64; other head sizes take the library's own choice). Left to itself the library
+    takes 4 waves only for grids that would not give every compute unit a workgroup, and splits the waves
+    when even that grid leaves compute units idle."""
+    if request.param == "ws":
+        monkeypatch.delenv("ATTN_PREFILL_WAVES", raising=False)
+        monkeypatch.setenv("ATTN_PREFILL_WSPLIT", "1")
+    else:
+        monkeypatch.setenv("ATTN_PREFILL_WAVES", request.param)
+        monkeypatch.setenv("ATTN_PREFILL_WSPLIT", "0")
     return request.param
 
 
@@ -211,6 +218,46 @@ def test_four_and_eight_wave_workgroups_agree_bitwise(case, monkeypatch):
                              out_dtype=torch.bfloat16)
     assert torch.equal(res["8"][0], res["4"][0])
     assert torch.equal(res["8"][1], res["4"][1])
+
+
+WAVE_SPLIT = [
+    # B, Tq, Tk, H, KV, hd, q_offset, window, causal, alibi, rope_base: head size 64, where grids too small
+    # for the chip split each 32-row block's key tiles over the 4 waves of its workgroup
+    (1, 512, 512, 8, 2, 64, 0, 0, 1, 0, 10000.0),      # the small workload's shape
+    (1, 700, 700, 8, 2, 64, 0, 0, 1, 0, 5e5),          # ragged end, 11 tiles on the last block
+    (2, 300, 300, 4, 4, 64, 0, 0, 1, 0, 10000.0),      # MHA
+    (1, 257, 257, 4, 2, 64, 0, 0, 1, 0, 0.0),          # one key past a tile: a share of one masked tile
+    (1, 200, 200, 8, 2, 64, 0, 0, 0, 0, 10000.0),      # not causal: every block walks all tiles
+    (1, 600, 600, 8, 2, 64, 0, 0, 1, 1, 0.0),          # causal ALiBi: each share walked from its top down
+    (1, 450, 450, 4, 4, 64, 0, 0, 1, 2, 10000.0),      # steeper slopes, MHA
+    (1, 700, 700, 8, 2, 64, 0, 200, 1, 0, 10000.0),    # sliding window: masked tiles at both ends
+    (1, 100, 900, 8, 2, 64, 800, 0, 1, 0, 10000.0),    # a chunk at the end of a prompt
+    (1, 1, 1500, 8, 2, 64, 1499, 0, 1, 1, 10000.0),    # one query token over 24 key tiles
+    (1, 64, 64, 8, 2, 64, 0, 0, 1, 0, 10000.0),        # one tile: three waves have no share
+    (1, 130, 130, 8, 2, 64, 0, 0, 1, 1, 10000.0),      # three tiles, the last holding two keys
+]
+
+
+@pytest.mark.parametrize("case", WAVE_SPLIT, ids=lambda c: "B%dTq%dTk%dH%dKV%dhd%d_off%d_w%d_c%d_a%d_b%g" % c)
+def test_wave_split_workgroups(case, monkeypatch):
+    """The 4 waves of a workgroup walk four shares of a block's key tiles and merge their running max,
+    denominator and output through LDS: against the oracle to the bf16 bar (fp32 output), and against the
+    unsplit 4-wave kernel (the same sums in another order) to the same bar."""
+    B, Tq, Tk, H, KV, hd, off, win, causal, alibi, base = case
+    q, k, v = W.random_prefill(4500 + Tk + off, B, Tk, H, KV, hd)
+    q = q[:, :, off:off + Tq].contiguous()
+    monkeypatch.delenv("ATTN_PREFILL_WAVES", raising=False)
+    monkeypatch.setenv("ATTN_PREFILL_WSPLIT", "1")
+    check_prefill(q, k, v, pos0=5, rope_base=base, causal=bool(causal), alibi=alibi, q_offset=off, window=win,
+                  label="wave split")
+    kw = dict(pos0=5, rope_base=base, causal=bool(causal), alibi=alibi, q_offset=off, window=win,
+              out_dtype=torch.bfloat16)
+    split = gpu_prefill(q, k, v, **kw)
+    monkeypatch.setenv("ATTN_PREFILL_WSPLIT", "0")
+    monkeypatch.setenv("ATTN_PREFILL_WAVES", "4")
+    plain = gpu_prefill(q, k, v, **kw)
+    assert (split[0].float() - plain[0].float()).abs().max().item() <= TOL[torch.bfloat16]
+    assert (split[1] - plain[1]).abs().max().item() <= LSE_TOL[torch.bfloat16]
 
 
 def test_chunked_alibi_prefill_equals_full_prefill_bitwise():

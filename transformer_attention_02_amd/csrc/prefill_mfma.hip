@@ -11,7 +11,10 @@
 //     packing), so every K/V tile staged in LDS serves 256 query rows. A grid
 //     that would not give every compute unit a workgroup runs 4-wave
 //     workgroups instead (half the rows each, 80 KiB of LDS, two per compute
-//     unit): twice as many workgroups share out the same work.
+//     unit): twice as many workgroups share out the same work. When even
+//     that grid leaves compute units idle (head size 64), the 4 waves of a
+//     workgroup take the same 32 rows of one head and split their key tiles
+//     four ways instead, merging the four partial states at the end.
 //   * A wave owns 32 query rows of one head and computes S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16. In the 32x32 accumulator a lane holds one
 //     query (column) and 16 keys (rows), so the row max and row sum are
@@ -293,18 +296,29 @@ struct WaveState {
 };
 
 // LDS buffer I of one kernel instance: with 8 waves, stage I of K then V;
-// with 4 waves, K buffer I (I = 0, 1) or V buffer I - 2 (I = 2, 3, 4).
-template <int HD, int NW, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW, int I>
+// with 4 waves, K buffer I (I = 0, 1) or V buffer I - 2 (I = 2, 3, 4). With
+// wave-split workgroups (WS) every wave owns such a set of five.
+template <int HD, int NW, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW, bool WS, int I>
 __device__ __forceinline__ unsigned char* lds_buf() {
-  __shared__ __attribute__((aligned(16))) unsigned char b[NW == 8 ? Cfg<HD>::STAGE : Cfg<HD>::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char b[(NW == 8 ? Cfg<HD>::STAGE : Cfg<HD>::K_BYTES) * (WS ? NW : 1)];
   return b;
 }
 
-template <int HD, int NW, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW>
+// WS (wave-split workgroups, for grids far too small to fill the chip): the
+// 4 waves of a workgroup own the same 32 query rows of one head and split the
+// block's key tiles four ways, each wave walking its share through its own
+// LDS ring with no workgroup barrier per step (one wave per SIMD, so none
+// waits on another's issue). Four times as many workgroups then spread over
+// idle compute units, and the longest walk is a quarter as long. The four
+// partial online-softmax states (running max, denominator, unnormalised O)
+// are merged through LDS at the end, the way the block recurrence of the
+// pages' tiled pass merges key blocks.
+template <int HD, int NW, bool ALIBI, bool CAUSAL, bool OUT_BF16, bool WINDOW, bool WS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   using C = Cfg<HD>;
   constexpr int NT = NW * 64;
+  static_assert(!WS || NW == 4, "wave-split workgroups have 4 waves");
   // Each buffer is its own LDS object, so the compiler can tell that the DMA
   // into one cannot alias the reads of another, and does not wait for the
   // in-flight tile before reading.
@@ -315,10 +329,11 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   //    step j+1); 80 KiB in all, so two workgroups share a compute unit.
   static_assert(NW == 8 || NW == 4, "8- or 4-wave workgroups");
   static_assert(C::K_BYTES == C::V_BYTES, "K and V buffers are interchangeable");
-#define LB(I) (lds_buf<HD, NW, ALIBI, CAUSAL, OUT_BF16, WINDOW, (I)>())
-
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+// buffer I of this wave (WS) or of the workgroup; LBW(W, I): buffer I of wave W
+#define LBW(W, I) (lds_buf<HD, NW, ALIBI, CAUSAL, OUT_BF16, WINDOW, WS, (I)>() + (WS ? (W) * C::K_BYTES : 0))
+#define LB(I) LBW(wave, I)
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hf = lane >> 5;
@@ -351,7 +366,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
 
   const int head = kvh * a.group + hc * gm.hpw + (wave % gm.hpw);
   const int q0 = qb * gm.bm;
-  const int qw0 = q0 + 32 * (wave / gm.hpw);
+  const int qw0 = WS ? q0 : q0 + 32 * (wave / gm.hpw);
   const bool wave_active = qw0 < a.Tq;
 
   const long kvoff = ((long)b * a.KV + kvh) * (long)a.Tk * HD;
@@ -362,8 +377,16 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // key some row of the workgroup sees: up to the last row's own token
   // (causal), from the first row's window start (sliding window).
   const int tq0 = a.q_off + q0, tq_last = a.q_off + q_last;
-  const int nkt = CAUSAL ? (tq_last / BN + 1) : (a.Tk + BN - 1) / BN;
-  const int kt_begin = WINDOW ? max(0, tq0 - a.window + 1) / BN : 0;
+  const int nkt_wg = CAUSAL ? (tq_last / BN + 1) : (a.Tk + BN - 1) / BN;
+  const int kt_begin_wg = WINDOW ? max(0, tq0 - a.window + 1) / BN : 0;
+  // This wave's tiles [kt_begin, nkt): the workgroup's, or with WS the w-th
+  // of four consecutive shares (the first ones one tile longer; possibly none)
+  int kt_begin = kt_begin_wg, nkt = nkt_wg;
+  if constexpr (WS) {
+    const int tot = nkt_wg - kt_begin_wg, q4 = tot / 4, r4 = tot % 4;
+    kt_begin = kt_begin_wg + wave * q4 + min(wave, r4);
+    nkt = kt_begin + q4 + (wave < r4 ? 1 : 0);
+  }
 
   // Causal ALiBi walks the key tiles from the last one down: each row meets
   // its largest bias (the keys nearest its token) first, so its running max
@@ -380,13 +403,17 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
                    : (P % 3 == 0 ? LB(2) : (P % 3 == 1 ? LB(3) : LB(4)));
   };
   // The first K/V tile streams in during the Q set-up.
-  Dma<HD, NW> dma;
-  dma.init(wave, lane);
-  dma.issue(Kg, Vg, REV ? nkt - 1 : kt_begin, a.Tk, kbuf(0), vbuf(0), wave);
+  // (with WS each wave moves whole tiles into its own ring)
+  constexpr int DW = WS ? 1 : NW;
+  const int dwave = WS ? 0 : wave;
+  Dma<HD, DW> dma;
+  dma.init(dwave, lane);
+  if (!WS || nkt > kt_begin) dma.issue(Kg, Vg, REV ? nkt - 1 : kt_begin, a.Tk, kbuf(0), vbuf(0), dwave);
   // V of the tile before the first one (buffer 2) is zeroed and the pending
   // probabilities start at zero, so the first tile's deferred product adds
   // exact zeros.
-  for (int e = tid; e < C::V_BYTES / 16; e += NT) reinterpret_cast<uint4*>(vbuf(2))[e] = make_uint4(0, 0, 0, 0);
+  for (int e = WS ? lane : tid; e < C::V_BYTES / 16; e += WS ? 64 : NT)
+    reinterpret_cast<uint4*>(vbuf(2))[e] = make_uint4(0, 0, 0, 0);
 
   WaveState<HD, ALIBI, CAUSAL, WINDOW> ws;
   ws.qi = a.q_off + qw0 + n;
@@ -427,7 +454,8 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     constexpr int TPT = (HD / 2) * TBM / NT;
     static_assert((HD / 2) * TBM * sizeof(float2) <= (NW == 8 ? C::STAGE : C::K_BYTES), "table fits");
     const bool table = a.rope && gm.bm == TBM;
-    float2* cs = reinterpret_cast<float2*>(kbuf(1));  // [HD/2][bm]
+    // (the table is shared: with WS it sits in wave 0's K buffer 1)
+    float2* cs = reinterpret_cast<float2*>(WS ? LBW(0, 1) : kbuf(1));  // [HD/2][bm]
     if (table) {
       double fr[TPT];
 #pragma unroll
@@ -487,7 +515,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // pprev owes its V^T product. Without a window every active wave runs the
   // first tile, so this starts true (the zero operands of "tile -1" are
   // harmless); with a window a wave may skip the first tiles and starts false.
-  bool pending = !WINDOW && !REV;
+  bool pending = !WINDOW && !REV && (!WS || nkt > kt_begin);
   auto step = [&](int kt, auto mask_tag, auto phase_tag, auto set_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(phase_tag)::value;  // walk step % 6
@@ -496,9 +524,9 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     unsigned char* prv = vbuf(P + 5);
     const int k0 = kt * BN;
     if constexpr (REV) {
-      if (kt > kt_begin) dma.issue(Kg, Vg, kt - 1, a.Tk, kbuf(P + 1), vbuf(P + 1), wave);
+      if (kt > kt_begin) dma.issue(Kg, Vg, kt - 1, a.Tk, kbuf(P + 1), vbuf(P + 1), dwave);
     } else {
-      if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.Tk, kbuf(P + 1), vbuf(P + 1), wave);
+      if (kt + 1 < nkt) dma.issue(Kg, Vg, kt + 1, a.Tk, kbuf(P + 1), vbuf(P + 1), dwave);
     }
     // in a masked tile a wave may be past its last visible key (causal) or
     // before its first one (sliding window)
@@ -520,8 +548,9 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       ws.pv((LdsBytes)prv, ws.pprev);
       pending = false;
     }
+    // (with WS only this wave reads and refills its ring: its own wait is enough)
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if constexpr (!WS) __syncthreads();
   };
   using F = std::integral_constant<bool, false>;
   using M = std::integral_constant<bool, true>;
@@ -608,8 +637,10 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       if (i + 3 < total) step(nkt - 4 - i, F{}, P3{}, S0{});
       if (i + 4 < total) step(nkt - 5 - i, F{}, P4{}, S0{});
     }
-    // the last step took tile kt_begin = 0, which every row sees
-    pending = true;
+    // the last step took tile kt_begin = 0, which every row sees; with WS a
+    // wave that skipped every tile of its share still owes only the zeros its
+    // operands started as
+    pending = total > 0;
   } else {
   if constexpr (WINDOW) {
     // tiles at the window's start, up to the first round boundary at or after
@@ -639,9 +670,53 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   }
   masked_rounds(nkt);
   }
-  if (!wave_active) return;
   // the last tile's V^T product (no DMA is in flight any more)
-  if (pending) ws.pv((LdsBytes)vbuf((nkt - 1 - kt_begin) % 3), ws.pprev);
+  if (wave_active && pending) ws.pv((LdsBytes)vbuf((nkt - 1 - kt_begin) % 3), ws.pprev);
+  if constexpr (WS) {
+    // Waves 1-3 leave their state in their own K buffers (O: HD/2 registers x
+    // 64 lanes x 4 bytes, one buffer; the running max and denominator in the
+    // other), and wave 0 merges the four and writes the rows.
+    static_assert((HD / 2) * 64 * 4 == C::K_BYTES, "one wave's O fills one buffer");
+    if (wave > 0) {
+      float* xo = reinterpret_cast<float*>(LB(0));
+      float* xm = reinterpret_cast<float*>(LB(1));
+#pragma unroll
+      for (int mb = 0; mb < HD / 32; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(mb * 16 + r) * 64 + lane] = ws.oacc[mb][r];
+      xm[lane] = ws.m_run;
+      xm[64 + lane] = ws.l_run;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    auto xo_of = [&](int w) __attribute__((always_inline)) {
+      return reinterpret_cast<const float*>(w == 1 ? LBW(1, 0) : (w == 2 ? LBW(2, 0) : LBW(3, 0)));
+    };
+    auto xm_of = [&](int w) __attribute__((always_inline)) {
+      return reinterpret_cast<const float*>(w == 1 ? LBW(1, 1) : (w == 2 ? LBW(2, 1) : LBW(3, 1)));
+    };
+    // O and l of each share are relative to that share's own running max
+    float mx = ws.m_run;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, xm_of(w)[lane]);
+    const float mr = mx == -INFINITY ? 0.f : mx;
+    const float a0 = __builtin_amdgcn_exp2f(ws.m_run - mr);
+#pragma unroll
+    for (int mb = 0; mb < HD / 32; ++mb) ws.oacc[mb] *= a0;
+    ws.l_run *= a0;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float aw = __builtin_amdgcn_exp2f(xm_of(w)[lane] - mr);
+      const float* xo = xo_of(w);
+#pragma unroll
+      for (int mb = 0; mb < HD / 32; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ws.oacc[mb][r] = fmaf(xo[(mb * 16 + r) * 64 + lane], aw, ws.oacc[mb][r]);
+      ws.l_run = fmaf(xm_of(w)[64 + lane], aw, ws.l_run);
+    }
+    ws.m_run = mx;
+  }
+  if (!wave_active) return;
 
   const float l_tot = ws.l_run + xhalf(ws.l_run);
   const float inv_l = 1.0f / l_tot;
@@ -712,13 +787,15 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   if (qi >= a.Tq) return;
   if (a.lse && hf == 0) a.lse[((long)b * a.H + head) * a.Tq + qi] = (ws.m_run + log2f(l_tot)) * 0.69314718055994531f;
 #undef LB
+#undef LBW
 }
 
+// nw = 0: the wave-split grid (one head and 32 query rows per workgroup)
 GridMap make_grid(const PrefillArgs& a, int nw) {
   GridMap gm;
-  gm.hpw = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
+  gm.hpw = nw == 0 ? 1 : (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
   gm.hchunks = a.group / gm.hpw;
-  gm.bm = 32 * (nw / gm.hpw);
+  gm.bm = nw == 0 ? 32 : 32 * (nw / gm.hpw);
   gm.nqb = (a.Tq + gm.bm - 1) / gm.bm;
   gm.units = a.B * a.KV * gm.hchunks;
   gm.xcd_aware = (gm.units % 8) == 0;
@@ -732,27 +809,28 @@ GridMap make_grid(const PrefillArgs& a, int nw) {
   return gm;
 }
 
-template <int HD, int NW, bool ALIBI, bool CAUSAL, bool WINDOW>
+template <int HD, int NW, bool ALIBI, bool CAUSAL, bool WINDOW, bool WS>
 void launch_out(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
   if (a.out_bf16) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, NW, ALIBI, CAUSAL, true, WINDOW>), grid, dim3(NW * 64), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, NW, ALIBI, CAUSAL, true, WINDOW, WS>), grid, dim3(NW * 64), 0, s, a, gm);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<HD, NW, ALIBI, CAUSAL, false, WINDOW>), grid, dim3(NW * 64), 0, s, a, gm);
+    hipLaunchKernelGGL((prefill_mfma_kernel<HD, NW, ALIBI, CAUSAL, false, WINDOW, WS>), grid, dim3(NW * 64), 0, s, a,
+                       gm);
   }
 }
 
 // The sliding window is a separate instance (causal only), so the plain
 // kernels carry none of its masking or tile-skipping code.
-template <int HD, int NW>
+template <int HD, int NW, bool WS>
 void launch_hd(const PrefillArgs& a, const GridMap& gm, dim3 grid, hipStream_t s) {
   if (a.alibi) {
-    if (a.window > 0) launch_out<HD, NW, true, true, true>(a, gm, grid, s);
-    else if (a.causal) launch_out<HD, NW, true, true, false>(a, gm, grid, s);
-    else launch_out<HD, NW, true, false, false>(a, gm, grid, s);
+    if (a.window > 0) launch_out<HD, NW, true, true, true, WS>(a, gm, grid, s);
+    else if (a.causal) launch_out<HD, NW, true, true, false, WS>(a, gm, grid, s);
+    else launch_out<HD, NW, true, false, false, WS>(a, gm, grid, s);
   } else {
-    if (a.window > 0) launch_out<HD, NW, false, true, true>(a, gm, grid, s);
-    else if (a.causal) launch_out<HD, NW, false, true, false>(a, gm, grid, s);
-    else launch_out<HD, NW, false, false, false>(a, gm, grid, s);
+    if (a.window > 0) launch_out<HD, NW, false, true, true, WS>(a, gm, grid, s);
+    else if (a.causal) launch_out<HD, NW, false, true, false, WS>(a, gm, grid, s);
+    else launch_out<HD, NW, false, false, false, WS>(a, gm, grid, s);
   }
 }
 
@@ -779,25 +857,46 @@ int pick_waves(const PrefillArgs& a) {
   return (long)gm.units * gm.nqb < device_cus() ? 4 : 8;
 }
 
+// Wave-split workgroups (head size 64: four rings fill the 160 KiB of LDS)
+// when the 4-wave grid leaves compute units idle, the wave-split grid fits
+// the compute units and some block walks more than four key tiles.
+// ATTN_PREFILL_WSPLIT=0 or 1 forces the choice at head size 64 (for tests).
+bool pick_wsplit(const PrefillArgs& a) {
+  if (a.hd != 64) return false;
+  if (const char* e = getenv("ATTN_PREFILL_WSPLIT")) {
+    if (e[0] == '0' && e[1] == 0) return false;
+    if (e[0] == '1' && e[1] == 0) return true;
+  }
+  if (getenv("ATTN_PREFILL_WAVES")) return false;  // a forced workgroup size keeps its kernel
+  const GridMap g4 = make_grid(a, 4), gw = make_grid(a, 0);
+  const int last = a.causal ? a.q_off + a.Tq - 1 : a.Tk - 1;  // the last key any row sees
+  return (long)g4.units * g4.nqb < device_cus() && (long)gw.units * gw.nqb <= device_cus() && last >= 4 * BN;
+}
+
 }  // namespace
 
 bool prefill_mfma_supported(const PrefillArgs& a, int bf16) {
   if (!bf16 || (a.hd != 64 && a.hd != 128)) return false;
   if ((long)a.Tk * a.hd * 2 >= (1L << 31)) return false;  // buffer descriptors hold 32-bit sizes
-  const GridMap gm = make_grid(a, 4);  // (the 4-wave grid is the larger one)
+  const GridMap gm = make_grid(a, 0);  // (the wave-split grid is the largest)
   return (long)gm.units * gm.nqb < (1L << 31);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
+  if (pick_wsplit(a)) {
+    const GridMap gm = make_grid(a, 0);
+    launch_hd<64, 4, true>(a, gm, dim3((unsigned)(gm.units * gm.nqb)), s);
+    return hipGetLastError();
+  }
   const int nw = pick_waves(a);
   const GridMap gm = make_grid(a, nw);
   const dim3 grid((unsigned)(gm.units * gm.nqb));
   if (a.hd == 128) {
-    if (nw == 8) launch_hd<128, 8>(a, gm, grid, s);
-    else launch_hd<128, 4>(a, gm, grid, s);
+    if (nw == 8) launch_hd<128, 8, false>(a, gm, grid, s);
+    else launch_hd<128, 4, false>(a, gm, grid, s);
   } else {
-    if (nw == 8) launch_hd<64, 8>(a, gm, grid, s);
-    else launch_hd<64, 4>(a, gm, grid, s);
+    if (nw == 8) launch_hd<64, 8, false>(a, gm, grid, s);
+    else launch_hd<64, 4, false>(a, gm, grid, s);
   }
   return hipGetLastError();
 }
