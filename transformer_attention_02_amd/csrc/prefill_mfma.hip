@@ -330,7 +330,16 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   static_assert(NW == 8 || NW == 4, "8- or 4-wave workgroups");
   static_assert(C::K_BYTES == C::V_BYTES, "K and V buffers are interchangeable");
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // (uniform across the wave: the LDS destination of a DMA must be, and the
+  // compiler otherwise wraps every DMA in a loop over the lanes' values)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#if defined(__HIP_DEVICE_COMPILE__)
+  // The scalar kernel arguments the set-up needs are requested together, so
+  // their memory latency is paid once rather than once per dependent use.
+  asm volatile("" ::"s"(gm.units), "s"(gm.nqb), "s"(gm.ugroup), "s"(gm.xcd_aware), "s"(gm.hchunks), "s"(gm.hpw),
+               "s"(gm.bm), "s"(a.KV), "s"(a.group), "s"(a.Tq), "s"(a.Tk), "s"(a.H), "s"(a.q_off), "s"(a.k),
+               "s"(a.v), "s"(a.q));
+#endif
 // buffer I of this wave (WS) or of the workgroup; LBW(W, I): buffer I of wave W
 #define LBW(W, I) (lds_buf<HD, NW, ALIBI, CAUSAL, OUT_BF16, WINDOW, WS, (I)>() + (WS ? (W) * C::K_BYTES : 0))
 #define LB(I) LBW(wave, I)
