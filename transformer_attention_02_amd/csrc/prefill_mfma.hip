@@ -682,11 +682,13 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // the last tile's V^T product (no DMA is in flight any more)
   if (wave_active && pending) ws.pv((LdsBytes)vbuf((nkt - 1 - kt_begin) % 3), ws.pprev);
   if constexpr (WS) {
-    // Waves 1-3 leave their state in their own K buffers (O: HD/2 registers x
+    // Every wave leaves its state in its own K buffers (O: HD/2 registers x
     // 64 lanes x 4 bytes, one buffer; the running max and denominator in the
-    // other), and wave 0 merges the four and writes the rows.
+    // other); then each wave merges the four states for a quarter of the head
+    // dimensions (accumulator registers wave*HD/8 .. +HD/8 in the order
+    // 16 mb + r) and writes that quarter of every row.
     static_assert((HD / 2) * 64 * 4 == C::K_BYTES, "one wave's O fills one buffer");
-    if (wave > 0) {
+    {
       float* xo = reinterpret_cast<float*>(LB(0));
       float* xm = reinterpret_cast<float*>(LB(1));
 #pragma unroll
@@ -697,33 +699,60 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       xm[64 + lane] = ws.l_run;
     }
     __syncthreads();
-    if (wave > 0) return;
     auto xo_of = [&](int w) __attribute__((always_inline)) {
-      return reinterpret_cast<const float*>(w == 1 ? LBW(1, 0) : (w == 2 ? LBW(2, 0) : LBW(3, 0)));
+      return reinterpret_cast<const float*>(w == 0 ? LBW(0, 0) : (w == 1 ? LBW(1, 0) : (w == 2 ? LBW(2, 0) : LBW(3, 0))));
     };
     auto xm_of = [&](int w) __attribute__((always_inline)) {
-      return reinterpret_cast<const float*>(w == 1 ? LBW(1, 1) : (w == 2 ? LBW(2, 1) : LBW(3, 1)));
+      return reinterpret_cast<const float*>(w == 0 ? LBW(0, 1) : (w == 1 ? LBW(1, 1) : (w == 2 ? LBW(2, 1) : LBW(3, 1))));
     };
     // O and l of each share are relative to that share's own running max
-    float mx = ws.m_run;
+    float mw[4], aw[4];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, xm_of(w)[lane]);
-    const float mr = mx == -INFINITY ? 0.f : mx;
-    const float a0 = __builtin_amdgcn_exp2f(ws.m_run - mr);
-#pragma unroll
-    for (int mb = 0; mb < HD / 32; ++mb) ws.oacc[mb] *= a0;
-    ws.l_run *= a0;
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const float aw = __builtin_amdgcn_exp2f(xm_of(w)[lane] - mr);
-      const float* xo = xo_of(w);
-#pragma unroll
-      for (int mb = 0; mb < HD / 32; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ws.oacc[mb][r] = fmaf(xo[(mb * 16 + r) * 64 + lane], aw, ws.oacc[mb][r]);
-      ws.l_run = fmaf(xm_of(w)[64 + lane], aw, ws.l_run);
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = xm_of(w)[lane];
+      mx = fmaxf(mx, mw[w]);
     }
-    ws.m_run = mx;
+    const float mr = mx == -INFINITY ? 0.f : mx;
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      aw[w] = __builtin_amdgcn_exp2f(mw[w] - mr);
+      l = fmaf(xm_of(w)[64 + lane], aw[w], l);
+    }
+    const float l_tot = l + xhalf(l);
+    const float inv_l = 1.0f / l_tot;
+    constexpr int QR = HD / 8;
+    float o[QR];
+#pragma unroll
+    for (int i = 0; i < QR; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* xo = xo_of(w) + wave * QR * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < QR; ++i) o[i] = fmaf(xo[i * 64], aw[w], o[i]);
+    }
+    const int qi = qw0 + n;
+    if (wave_active && qi < a.Tq) {
+      const long orow = (((long)b * a.H + head) * a.Tq + qi) * HD;
+#pragma unroll
+      for (int g = 0; g < QR / 4; ++g) {
+        // registers f .. f+3 hold dims d .. d+3 of the lane's row
+        const int f = wave * QR + 4 * g;
+        const int d = 32 * (f / 16) + 8 * ((f % 16) / 4) + 4 * hf;
+        const float o0 = o[4 * g] * inv_l, o1 = o[4 * g + 1] * inv_l, o2 = o[4 * g + 2] * inv_l, o3 = o[4 * g + 3] * inv_l;
+        if constexpr (OUT_BF16) {
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d) =
+              u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + d) = make_float4(o0, o1, o2, o3);
+        }
+      }
+      if (wave == 0 && a.lse && hf == 0)
+        a.lse[((long)b * a.H + head) * a.Tq + qi] = (mx + log2f(l_tot)) * 0.69314718055994531f;
+    }
+    return;
   }
   if (!wave_active) return;
 
