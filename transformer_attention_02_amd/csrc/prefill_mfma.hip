@@ -338,7 +338,7 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   // their memory latency is paid once rather than once per dependent use.
   asm volatile("" ::"s"(gm.units), "s"(gm.nqb), "s"(gm.ugroup), "s"(gm.xcd_aware), "s"(gm.hchunks), "s"(gm.hpw),
                "s"(gm.bm), "s"(a.KV), "s"(a.group), "s"(a.Tq), "s"(a.Tk), "s"(a.H), "s"(a.q_off), "s"(a.k),
-               "s"(a.v), "s"(a.q));
+               "s"(a.v), "s"(a.q), "s"(a.rope), "s"(a.pos0));
 #endif
 // buffer I of this wave (WS) or of the workgroup; LBW(W, I): buffer I of wave W
 #define LBW(W, I) (lds_buf<HD, NW, ALIBI, CAUSAL, OUT_BF16, WINDOW, WS, (I)>() + (WS ? (W) * C::K_BYTES : 0))
@@ -457,18 +457,29 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
       for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
     }
     // The table fits only with 4 heads per workgroup (bm = 8 * NW rows), so a
-    // thread fills HD / 16 entries, pairs tid / bm + 8i; their frequencies are
-    // all requested before the first is used (one memory latency, not HD / 16).
+    // thread fills HD / 16 entries, pairs tid / bm + 8i: with 8 waves pair
+    // wave + 8i, with 4 waves 2 wave + hf + 8i. Those indices are uniform over
+    // a wave (or half-wave), so the frequencies come by scalar loads, all
+    // requested before the first is used.
     constexpr int TBM = 8 * NW;
     constexpr int TPT = (HD / 2) * TBM / NT;
     static_assert((HD / 2) * TBM * sizeof(float2) <= (NW == 8 ? C::STAGE : C::K_BYTES), "table fits");
     const bool table = a.rope && gm.bm == TBM;
     // (the table is shared: with WS it sits in wave 0's K buffer 1)
     float2* cs = reinterpret_cast<float2*>(WS ? LBW(0, 1) : kbuf(1));  // [HD/2][bm]
-    if (table) {
-      double fr[TPT];
+    // (loaded whether or not the table is built: kernel arguments, always valid)
+    double fr[TPT];
+    const int pw = NW == 8 ? wave : 2 * wave;
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) fr[i] = a.freqs.rev[(tid + i * NT) / TBM];
+    for (int i = 0; i < TPT; ++i) {
+      if constexpr (NW == 8) {
+        fr[i] = a.freqs.rev[pw + 8 * i];
+      } else {
+        const double f0 = a.freqs.rev[pw + 8 * i], f1 = a.freqs.rev[pw + 1 + 8 * i];
+        fr[i] = hf ? f1 : f0;
+      }
+    }
+    if (table) {
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
         const int e = tid + i * NT;
