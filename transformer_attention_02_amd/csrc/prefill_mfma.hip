@@ -330,9 +330,11 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
   static_assert(NW == 8 || NW == 4, "8- or 4-wave workgroups");
   static_assert(C::K_BYTES == C::V_BYTES, "K and V buffers are interchangeable");
   const int tid = threadIdx.x;
-  // (uniform across the wave: the LDS destination of a DMA must be, and the
-  // compiler otherwise wraps every DMA in a loop over the lanes' values)
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // (with WS the wave index picks each wave's tile range, hence every DMA's
+  // buffer descriptor, which must be uniform: as a per-lane value the compiler
+  // wraps each DMA in a loop over the lanes' values. Elsewhere it stays a
+  // vector value: as a scalar one the 4-wave hd-128 instances spill registers.)
+  const int wave = WS ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
 #if defined(__HIP_DEVICE_COMPILE__)
   // The scalar kernel arguments the set-up needs are requested together, so
   // their memory latency is paid once rather than once per dependent use.
