@@ -190,8 +190,11 @@ struct WaveState {
   // copy at the end); in the six-step clean loop, 1 reads pprev and writes
   // palt, 2 reads palt and writes pprev, so no copy is needed and pprev holds
   // the due operands again after every six steps.
+  // (full: every key of the tile is visible to every row of the wave, so a
+  // masked step skips the mask; rounds of masked steps cover such tiles too)
   template <bool MASK, int SET = 0>
-  __device__ __forceinline__ void softmax_pv(const f32x16& sa, const f32x16& sb, int k0, LdsBytes vprev) {
+  __device__ __forceinline__ void softmax_pv(const f32x16& sa, const f32x16& sb, int k0, LdsBytes vprev,
+                                             bool full = false) {
     bf16x8(&pin)[4] = SET == 2 ? palt : pprev;
     bf16x8(&pout)[4] = SET == 1 ? palt : pprev;
     const int hf = lane >> 5;
@@ -220,7 +223,7 @@ struct WaveState {
         t[i] = x;
       }
     }
-    if constexpr (MASK) {
+    if (MASK && !full) {
       // register i holds key k0 + 8hf + c_i (c_i a constant): it is visible when
       // lo <= c_i <= hi, the per-lane limits folding the causal bound (key <= qi),
       // the sequence end (key < Tk) and the window start (key > qi - window)
@@ -555,13 +558,17 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
     const int tw0 = a.q_off + qw0;
     const bool run = wave_active && !(MASK && ((CAUSAL && k0 > tw0 + 31) ||
                                                (WINDOW && k0 + BN - 1 < tw0 - a.window + 1)));
+    // every key of the tile visible to all 32 rows: before the first row's
+    // token, inside the sequence, inside the last row's window
+    const bool full = MASK && (!CAUSAL || k0 + BN - 1 <= tw0) && k0 + BN <= a.Tk &&
+                      (!WINDOW || k0 >= tw0 + 32 - a.window);
     if (run) {
       f32x16 sa, sb;
       ws.scores((LdsBytes)cur, sa, sb);
       // A wave in its softmax + deferred-product phase gets issue priority
       // over a wave computing scores (measured: fewer cycles per tile).
       __builtin_amdgcn_s_setprio(1);
-      ws.template softmax_pv<MASK, SET>(sa, sb, k0, (LdsBytes)prv);
+      ws.template softmax_pv<MASK, SET>(sa, sb, k0, (LdsBytes)prv, full);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (MASK && (WINDOW || REV)) pending = true;
     } else if (MASK && pending) {
