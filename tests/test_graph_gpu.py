@@ -128,3 +128,19 @@ def test_graph_decode_steps():
         return {"o1": o1, "l1": l1, "qp": qp, "o2": o2, "l2": l2, "o3": o3, "l3": l3, "o4": o4, "l4": l4}
 
     _replay_and_compare(step, "decode")
+
+
+def test_graph_wave_split_prefill(monkeypatch):
+    """The small prefill's shape with the wave-split workgroups forced: the rotated-K pre-pass, then the kernel
+    whose four waves each walk a share of a block's key tiles and merge through LDS."""
+    monkeypatch.delenv("ATTN_PREFILL_WAVES", raising=False)
+    monkeypatch.setenv("ATTN_PREFILL_WSPLIT", "1")
+    w = W.SMALL_BF16
+    q, k, v = (t.cuda() for t in W.prefill_inputs(w))
+    ws, _ = bd.prefill_workspace(w.B, w.T, w.KV, w.hd, bd.ATTN_DTYPE_BF16, w.rope_base, "cuda")
+
+    def step():
+        o, lse = bd.prefill(q, k, v, rope_base=w.rope_base, out_dtype=torch.bfloat16, workspace=ws)
+        return {"o": o, "lse": lse}
+
+    _replay_and_compare(step, "wave-split prefill")
