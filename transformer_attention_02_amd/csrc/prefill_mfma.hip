@@ -461,8 +461,9 @@ void prefill_mfma_kernel(PrefillArgs a, GridMap gm) {
 #pragma unroll
       for (int s = 0; s < HD / 16; ++s) raw[s] = src[2 * s + hf];
     }
-    // The table fits only with 4 heads per workgroup (bm = 8 * NW rows), so a
-    // thread fills HD / 16 entries, pairs tid / bm + 8i: with 8 waves pair
+    // The table fits only when a workgroup owns bm = 8 * NW query rows (4
+    // heads per workgroup, or with WS one head's 32 rows), so a thread fills
+    // HD / 16 entries, pairs tid / bm + 8i: with 8 waves pair
     // wave + 8i, with 4 waves 2 wave + hf + 8i. Those indices are uniform over
     // a wave (or half-wave), so the frequencies come by scalar loads, all
     // requested before the first is used.
